@@ -1,0 +1,218 @@
+// Device building blocks for ROCmFPX block-quantized kernels on gfx950 (wave64).
+//
+// Page citations:
+//   [Strix-284B] lucebox.com, "DeepSeek V4 Flash: 284B model, up to 32 tok/s on
+//   AMD Ryzen AI MAX+ 395", section "ROCmFPX: fitting 284B weights into 128 GB":
+//   32-weight blocks of low-bit codes and a small scale, read directly from
+//   memory; the small codebook is expanded in registers with byte-permute
+//   instructions and fed to integer dot products without a separate gather.
+//   [evox3] soothill.io, "DeepSeek V4 Flash 0731 on evox3", table "The
+//   optimization ladder": H32 rotation of the expert input, shared across experts.
+//
+// Layout facts used here (the library's format, also stated in include/qmoe.h):
+//   - 2-bit plane word m of a block: (W_m >> 2k) & 0x03030303 = selectors of
+//     weights 16m+4k+0..3, i.e. of activation dword 4m+k.
+//   - FP3 bit-2 plane word H: (H >> g) & 0x01010101 = bit 2 of weights 4g+0..3.
+//   - FP4 nibble word w: (W_w >> 4h) & 0x0F0F0F0F = codes of weights 8w+4h+0..3,
+//     i.e. of activation dword 2w+h.
+//   - Row-planar rows: code planes of all blocks, FP3 high planes, scales.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qk {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  // v_perm_b32: result byte i = byte sel_i of the 8-byte value {hi, lo} (lo = bytes 0..3)
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);   // int8 x int8, int32 accumulate
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// E8M0: 2^(e-127). e >= 1 is a normal fp32 with exponent field e; e = 0 is the
+// subnormal 2^-127 (mantissa bit 22).
+__device__ __forceinline__ float e8m0_to_float(uint32_t e) {
+  return e ? __uint_as_float(e << 23) : __uint_as_float(0x00200000u);
+}
+
+template <int FMT> struct Fmt;
+template <> struct Fmt<2> { static constexpr int kLoWords = 2, kHi = 0, kScaleBytes = 2, kBlockBytes = 10, kCbWords = 1; };
+template <> struct Fmt<3> { static constexpr int kLoWords = 2, kHi = 1, kScaleBytes = 2, kBlockBytes = 14, kCbWords = 2; };
+template <> struct Fmt<4> { static constexpr int kLoWords = 4, kHi = 0, kScaleBytes = 1, kBlockBytes = 17, kCbWords = 4; };
+
+// Codebook of 2^bits int8 entries held as 1, 2 or 4 dwords.
+template <int FMT>
+__device__ __forceinline__ void load_codebook(const int8_t* cb, uint32_t w[4]) {
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(cb);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = (i < Fmt<FMT>::kCbWords) ? p[i] : 0u;
+}
+
+// NBL consecutive blocks of one row, starting at block b (row-planar layout).
+template <int FMT, int NBL>
+struct Blocks {
+  uint32_t lo[NBL][Fmt<FMT>::kLoWords];
+  uint32_t hi[NBL];
+  float s[NBL];
+
+  __device__ __forceinline__ void load(const uint8_t* row, int nb, int b) {
+    constexpr int LW = Fmt<FMT>::kLoWords;
+    const uint8_t* codes = row + (size_t)b * LW * 4;
+    if constexpr (LW * NBL == 4) {
+      uint4 v = *reinterpret_cast<const uint4*>(codes);
+      uint32_t t[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < NBL; ++i)
+#pragma unroll
+        for (int w = 0; w < LW; ++w) lo[i][w] = t[i * LW + w];
+    } else if constexpr (LW * NBL == 2) {
+      uint2 v = *reinterpret_cast<const uint2*>(codes);
+      lo[0][0] = v.x;
+      lo[0][1] = v.y;
+    } else {  // FP4, NBL = 2: 32 bytes
+      uint4 v0 = *reinterpret_cast<const uint4*>(codes);
+      uint4 v1 = *reinterpret_cast<const uint4*>(codes + 16);
+      lo[0][0] = v0.x; lo[0][1] = v0.y; lo[0][2] = v0.z; lo[0][3] = v0.w;
+      lo[NBL - 1][0] = v1.x; lo[NBL - 1][1] = v1.y; lo[NBL - 1][2] = v1.z; lo[NBL - 1][3] = v1.w;
+    }
+    const uint8_t* after_lo = row + (size_t)nb * LW * 4;
+    if constexpr (Fmt<FMT>::kHi) {
+      if constexpr (NBL == 2) {
+        uint2 h = *reinterpret_cast<const uint2*>(after_lo + (size_t)b * 4);
+        hi[0] = h.x;
+        hi[NBL - 1] = h.y;
+      } else {
+        hi[0] = *reinterpret_cast<const uint32_t*>(after_lo + (size_t)b * 4);
+      }
+    }
+    const uint8_t* sc = after_lo + (size_t)nb * 4 * Fmt<FMT>::kHi;
+    if constexpr (Fmt<FMT>::kScaleBytes == 2) {
+      if constexpr (NBL == 2) {
+        uint32_t w = *reinterpret_cast<const uint32_t*>(sc + (size_t)b * 2);
+        s[0] = half_bits_to_float(w & 0xFFFFu);
+        s[NBL - 1] = half_bits_to_float(w >> 16);
+      } else {
+        s[0] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(sc + (size_t)b * 2));
+      }
+    } else {
+      if constexpr (NBL == 2) {
+        uint32_t w = *reinterpret_cast<const uint16_t*>(sc + b);
+        s[0] = e8m0_to_float(w & 0xFFu);
+        s[NBL - 1] = e8m0_to_float(w >> 8);
+      } else {
+        s[0] = e8m0_to_float(sc[b]);
+      }
+    }
+  }
+
+  // Expand block i into 8 dwords of int8 weights; out[g] covers weights 4g..4g+3.
+  __device__ __forceinline__ void expand(int i, const uint32_t cb[4], uint32_t out[8]) const {
+    if constexpr (FMT == 2) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) out[4 * m + k] = perm(cb[0], cb[0], (lo[i][m] >> (2 * k)) & 0x03030303u);
+    } else if constexpr (FMT == 3) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int g = 4 * m + k;
+          const uint32_t sel = ((lo[i][m] >> (2 * k)) & 0x03030303u) | (((hi[i] >> g) & 0x01010101u) << 2);
+          out[g] = perm(cb[1], cb[0], sel);
+        }
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t sel = (lo[i][w] >> (4 * h)) & 0x0F0F0F0Fu;
+          const uint32_t s7 = sel & 0x07070707u;
+          const uint32_t a = perm(cb[1], cb[0], s7);           // entries 0..7
+          const uint32_t c = perm(cb[3], cb[2], s7);           // entries 8..15
+          const uint32_t m = ((sel >> 3) & 0x01010101u) * 0xFFu;
+          out[2 * w + h] = (c & m) | (a & ~m);
+        }
+    }
+  }
+};
+
+// int8 activations of NBL consecutive blocks.
+template <int NBL>
+struct Acts {
+  uint32_t q[NBL][8];
+  float d[NBL];
+  __device__ __forceinline__ void load(const int8_t* xq, const float* dx, int b) {
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) {
+      const uint4* p = reinterpret_cast<const uint4*>(xq + (size_t)(b + i) * 32);
+      uint4 a = p[0], c = p[1];
+      q[i][0] = a.x; q[i][1] = a.y; q[i][2] = a.z; q[i][3] = a.w;
+      q[i][4] = c.x; q[i][5] = c.y; q[i][6] = c.z; q[i][7] = c.w;
+      d[i] = dx[b + i];
+    }
+  }
+};
+
+__device__ __forceinline__ int block_dot(const uint32_t w[8], const uint32_t x[8]) {
+  int acc = 0;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) acc = dot4(w[g], x[g], acc);
+  return acc;
+}
+
+// Sum over groups of `lpr` adjacent lanes (lpr a power of two <= 64).
+__device__ __forceinline__ float group_sum(float v, int lpr) {
+  for (int m = lpr >> 1; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// int8 quantization of one 32-element activation block, bit-exact with the
+// CPU checker: optional H32 (butterflies h = 1,2,4,8,16, then * fp32 nearest
+// 1/sqrt(32)), amax, d = amax/127, id = 1/d (0 if d == 0),
+// q = clamp(rint(v*id), -127, 127). IEEE binary32, no contraction.
+__device__ __forceinline__ void quant_block32(float v[32], int rot, uint32_t q[8], float* d_out) {
+#pragma clang fp contract(off)
+  if (rot) {
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        if (!(j & h)) {
+          const float a = v[j], b = v[j + h];
+          v[j] = a + b;
+          v[j + h] = a - b;
+        }
+    const float c = __uint_as_float(0x3E3504F3u);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v[j] = v[j] * c;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  const float d = amax / 127.0f;
+  const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float r = rintf(v[4 * g + i] * id);
+      r = fminf(fmaxf(r, -127.0f), 127.0f);
+      w |= ((uint32_t)(int)r & 0xFFu) << (8 * i);
+    }
+    q[g] = w;
+  }
+  *d_out = d;
+}
+
+}  // namespace qk

@@ -1,0 +1,190 @@
+/*
+ * qmoe.h — C ABI of libqmoe: ROCmFPX block-quantized MoE layers on MI355X (gfx950).
+ *
+ * Page citations:
+ *   [Strix-284B] lucebox.com, "DeepSeek V4 Flash: 284B model, up to 32 tok/s on
+ *                AMD Ryzen AI MAX+ 395", sections "ROCmFPX: fitting 284B weights
+ *                into 128 GB" and "Decode: up to 32 tok/s".
+ *   [0731-Strix] lucebox.com, "Lucebox × Geometric: DeepSeek V4 Flash 0731
+ *                reaches 32.7 tok/s on AMD Strix Halo", sections "How the model
+ *                fits on AMD Strix Halo", "Lucebox Engine integration with
+ *                Geometric" and "Run with Lucebox Engine".
+ *   [evox3]      soothill.io, "DeepSeek V4 Flash 0731 on evox3", introduction and
+ *                table "The optimization ladder".
+ *
+ * Data formats (normative for both this library and its CPU checker):
+ *   A block is 32 consecutive weights of one row ([Strix-284B], ROCmFPX section).
+ *   FP2: 8 B of 2-bit codes + fp16 scale = 10 B (2.50 bpw).
+ *        Code of weight j: byte 4*(j>>4) + (j&3), bits 2*((j>>2)&3)..+1.
+ *   FP3: FP2-style plane of the low 2 code bits (8 B) + 4 B plane of bit 2
+ *        (weight j: byte j&3, bit j>>2) + fp16 scale = 14 B (3.50 bpw).
+ *   FP4: 16 B of nibbles (weight j: byte 4*(j>>3) + (j&3), bits 4*((j>>2)&1)..+3)
+ *        + E8M0 scale byte e (value 2^(e-127), e = 255 invalid) = 17 B (4.25 bpw).
+ *   Rows are row-planar: all code planes of the row (block-major), then the FP3
+ *   high planes, then the scales (little-endian fp16 or E8M0 bytes).
+ *   Codebooks: int8, 2^bits entries per (tensor, expert); dequantized weight =
+ *   scale * C[code] ([0731-Strix]: learned per-expert codebooks).
+ *   Activations: per 32-block, optional H32 (Sylvester FWHT, butterflies
+ *   h = 1..16, then * fp32(1/sqrt(32))), d = amax/127, q = clamp(rint(v/d)).
+ *
+ * Conventions:
+ *   - Every pointer argument of a launch entry point is a DEVICE pointer unless
+ *     the comment says host. The caller owns all memory; the library never
+ *     allocates, frees or keeps a pointer after the call returns, and never
+ *     synchronises the host.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Launch entry points are asynchronous on that stream.
+ *   - Every entry point returns a qmoe_status. Argument errors are detected on the
+ *     host before any launch ([0731-Strix] integration section: codebooks are
+ *     validated before serving starts; [evox3] introduction: an unsupported
+ *     rotation must fail at load, not mid-run). A message naming the argument is
+ *     available from qmoe_last_error() (thread-local).
+ *   - No C++ exception crosses this ABI.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QMOE_OK = 0,
+  QMOE_E_INVAL = -1,     /* NULL pointer, bad enum value, bad flag            */
+  QMOE_E_SHAPE = -2,     /* K % 32 != 0, q not in 1..4, topk not in 1..min(E,8) */
+  QMOE_E_FORMAT = -3,    /* unknown format or unsupported format/rotation pair */
+  QMOE_E_CODEBOOK = -4,  /* missing / truncated / mismatched codebook bytes     */
+  QMOE_E_SCALE = -5,     /* non-finite fp16 scale or E8M0 0xFF (pack)           */
+  QMOE_E_WORKSPACE = -6, /* workspace missing or smaller than required          */
+  QMOE_E_HIP = -7,       /* a HIP runtime call or launch failed                 */
+  QMOE_E_SIZE = -8       /* a weight buffer is smaller than its shape requires  */
+} qmoe_status;
+
+typedef enum { QMOE_FP2 = 2, QMOE_FP3 = 3, QMOE_FP4 = 4 } qmoe_format;
+
+/* Human-readable name of a status code (static string). */
+const char* qmoe_strerror(int status);
+/* Detail of the last error on this thread (static thread-local buffer). */
+const char* qmoe_last_error(void);
+/* ABI version (major * 100 + minor). */
+int qmoe_version(void);
+
+/* Bytes per 32-weight block: 10, 14, 17; 0 for an unknown format. */
+size_t qmoe_block_bytes(int fmt);
+/* rows * (k/32) * block bytes; 0 if k % 32 != 0 or the format is unknown. */
+size_t qmoe_packed_bytes(int fmt, int64_t rows, int64_t k);
+
+/* HOST (CPU only). Packs codes (host uint8 [rows*k], each < 2^bits) and scales
+ * (host; uint16 fp16 bits [rows*k/32] for FP2/FP3, uint8 E8M0 [rows*k/32] for
+ * FP4) into `out` (host, out_bytes >= qmoe_packed_bytes). Rejects codes out of
+ * range (QMOE_E_INVAL), non-finite fp16 or E8M0 0xFF scales (QMOE_E_SCALE). */
+int qmoe_pack(int fmt, int64_t rows, int64_t k, const uint8_t* codes,
+              const void* scales, void* out, size_t out_bytes);
+/* HOST. Inverse of qmoe_pack. */
+int qmoe_unpack(int fmt, int64_t rows, int64_t k, const void* packed,
+                size_t packed_bytes, uint8_t* codes, void* scales);
+
+/* One top-k SwiGLU MoE layer ([Strix-284B] ROCmFPX section: routed gate/up in
+ * the 2.5-bit format, down in the 3.5-bit format; [0731-Strix] run section:
+ * 256 experts, 6 routed). All pointers are device pointers.
+ *   gate, up: [E][inter][row_bytes(fmt, hidden)];  down: [E][hidden][row_bytes(fmt, inter)]
+ *   cb_*:     [E][2^bits(fmt)] int8
+ *   w_router: fp16 bits [E][hidden];  router_bias: fp64 [E] or NULL (= 0)
+ *   rot_gateup / rot_down: 0 = none, 1 = H32 on the input blocks of gate/up
+ *   (the token) or of down (the SwiGLU output). */
+typedef struct {
+  int32_t hidden, inter, n_experts, topk;
+  int32_t fmt_gate, fmt_up, fmt_down;
+  int32_t rot_gateup, rot_down;
+  const uint16_t* w_router; size_t w_router_bytes;
+  const double* router_bias;
+  const void* gate; size_t gate_bytes;
+  const void* up;   size_t up_bytes;
+  const void* down; size_t down_bytes;
+  const int8_t* cb_gate; size_t cb_gate_bytes;
+  const int8_t* cb_up;   size_t cb_up_bytes;
+  const int8_t* cb_down; size_t cb_down_bytes;
+} qmoe_layer;
+
+/* HOST check of a layer descriptor (no device access): shapes, formats,
+ * rotation flags, missing / truncated / mismatched weights and codebooks. */
+int qmoe_layer_check(const qmoe_layer* L);
+
+/* Bytes of device workspace needed by qmoe_route / qmoe_decode_layer /
+ * qmoe_prefill_layer for up to `max_tokens` tokens (0 on an invalid layer).
+ * The workspace must be zero-filled once before its first use; every call
+ * leaves its control words zero again on exit. Calls that share a workspace
+ * must be ordered (same stream or synchronised). */
+size_t qmoe_workspace_bytes(const qmoe_layer* L, int32_t max_tokens);
+
+/* Router only: logits in fp64 in a fixed order (per block sequential, then a
+ * stride-halving tree over blocks, + bias), top-k with ties to the lower id,
+ * ids ascending, softmax over the k selected logits. x: fp32 [ntok][hidden];
+ * idx: int32 [ntok][topk]; gate_w: fp32 [ntok][topk].
+ * ([Strix-284B] decode section: dedicated top-k / argsort routing kernels.) */
+int qmoe_route(const qmoe_layer* L, const float* x, int32_t ntok, int32_t* idx,
+               float* gate_w, void* ws, size_t ws_bytes, void* stream);
+
+/* Decode: q = 1..4 independent tokens (verification columns). Each packed
+ * block of every expert selected by any of the q tokens is read and expanded
+ * once and applied to each column routed to it ([Strix-284B] decode section).
+ * x: fp32 [q][hidden]; out: fp32 [q][hidden]. No host synchronisation. */
+int qmoe_decode_layer(const qmoe_layer* L, const float* x, int32_t q, float* out,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Prefill: ntok tokens through the layer, grouped by expert on the device
+ * ([evox3] ladder: layer-major prefill batching). x: fp32 [ntok][hidden];
+ * out: fp32 [ntok][hidden]. Deterministic: per token the expert outputs are
+ * combined in ascending expert id. */
+int qmoe_prefill_layer(const qmoe_layer* L, const float* x, int32_t ntok, float* out,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of qmoe_matvec for K = k and ncols columns. */
+size_t qmoe_matvec_workspace_bytes(int64_t k, int32_t ncols);
+
+/* Dense block-quantized matvec / small matmul: y[c][r] = sum_b s[r][b] d_c[b] P_c[r][b]
+ * for columns c < ncols (1..4), with x quantized per 32-block (rot 0 or 1).
+ * w: packed [rows][row_bytes]; cb: int8 [2^bits]; x: fp32 [ncols][k];
+ * y: fp32 [ncols][rows]. Each block is expanded once for all columns. */
+int qmoe_matvec(int fmt, int64_t rows, int64_t k, const void* w, size_t w_bytes,
+                const int8_t* cb, int32_t rot, const float* x, int32_t ncols,
+                float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Activation quantization only: x fp32 [n_vec][k] -> xq int8 [n_vec][k],
+ * dx fp32 [n_vec][k/32]. */
+int qmoe_quant_act(const float* x, int64_t n_vec, int64_t k, int32_t rot,
+                   int8_t* xq, float* dx, void* stream);
+
+/* Per-block exact integer sums P[r][b] = sum_j C[code] * xq[32b+j] (int32),
+ * through the same expansion and dot code as the layer kernels.
+ * xq: int8 [k]; P: int32 [rows][k/32]. */
+int qmoe_block_dots(int fmt, int64_t rows, int64_t k, const void* w, size_t w_bytes,
+                    const int8_t* cb, const int8_t* xq, int32_t* P, void* stream);
+
+/* Byte offsets of the internal buffers inside a layer workspace, so that a caller
+ * can inspect intermediate results (int8 activations, routing, SwiGLU outputs).
+ * Fields are byte offsets from the workspace start. */
+typedef struct {
+  size_t ctrl;        /* uint32 control words; word 0 = device error flags */
+  size_t xq;          /* int8  [max_tokens][hidden]                        */
+  size_t dx;          /* fp32  [max_tokens][hidden/32]                     */
+  size_t idx;         /* int32 [max_tokens][topk]                          */
+  size_t gw;          /* fp32  [max_tokens][topk]                          */
+  size_t logits;      /* fp64  [max_tokens][E]                             */
+  size_t plan;        /* decode plan: int32 U, ids[32], masks[32], fp32 w[32][4] */
+  size_t hq;          /* int8  [slots][inter]  (decode: slot = u*4 + t; prefill: pair) */
+  size_t dh;          /* fp32  [slots][inter/32]                           */
+  size_t group;       /* prefill grouping (counts, offsets, pairs, tiles)  */
+  size_t ypair;       /* fp32  [max_tokens][topk][hidden] (prefill)        */
+  size_t total;       /* == qmoe_workspace_bytes                           */
+} qmoe_ws_layout;
+
+int qmoe_workspace_layout(const qmoe_layer* L, int32_t max_tokens, qmoe_ws_layout* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMOE_H */

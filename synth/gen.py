@@ -118,7 +118,7 @@ class LayerSpec:
     @staticmethod
     def tiny(**kw) -> "LayerSpec":
         """A small layer of the same structure for fast tests."""
-        d = dict(hidden=128, inter=64, n_experts=8, topk=2)
+        d = dict(hidden=256, inter=256, n_experts=8, topk=2)
         d.update(kw)
         return LayerSpec(**d)
 
