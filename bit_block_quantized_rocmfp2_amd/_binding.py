@@ -48,6 +48,13 @@ class qmoe_ws_layout(ctypes.Structure):
 
 
 def _load():
+    # When torch is present it must load its HIP runtime first: libqmoe then binds
+    # to that already-loaded libamdhip64.so.7 instead of a second runtime copy,
+    # so device pointers and streams from torch are valid in the library.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libqmoe is not built ({LIB_PATH} missing); run __graft_entry__.build()")
     lib = ctypes.CDLL(LIB_PATH)

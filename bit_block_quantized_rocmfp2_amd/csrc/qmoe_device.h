@@ -178,8 +178,9 @@ __device__ __forceinline__ float group_sum(float v, int lpr) {
 // ---------------------------------------------------------------------------
 // int8 quantization of one 32-element activation block, bit-exact with the
 // CPU checker: optional H32 (butterflies h = 1,2,4,8,16, then * fp32 nearest
-// 1/sqrt(32)), amax, d = amax/127, id = 1/d (0 if d == 0),
-// q = clamp(rint(v*id), -127, 127). IEEE binary32, no contraction.
+// 1/sqrt(32)), amax, d = amax/127 (a zero or subnormal d stores the block as
+// d = 0, q = 0), id = 1/d, q = clamp(rint(v*id), -127, 127). IEEE binary32, no
+// contraction.
 __device__ __forceinline__ void quant_block32(float v[32], int rot, uint32_t q[8], float* d_out) {
 #pragma clang fp contract(off)
   if (rot) {
@@ -199,8 +200,11 @@ __device__ __forceinline__ void quant_block32(float v[32], int rot, uint32_t q[8
   float amax = 0.0f;
 #pragma unroll
   for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-  const float d = amax / 127.0f;
-  const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+  // a zero or subnormal scale (1/d would overflow) stores the block as zero
+  const float d0 = amax / 127.0f;
+  const bool normal = d0 >= __uint_as_float(0x00800000u);   // 2^-126
+  const float d = normal ? d0 : 0.0f;
+  const float id = normal ? 1.0f / d0 : 0.0f;
 #pragma unroll
   for (int g = 0; g < 8; ++g) {
     uint32_t w = 0;

@@ -25,7 +25,8 @@
  *   Codebooks: int8, 2^bits entries per (tensor, expert); dequantized weight =
  *   scale * C[code] ([0731-Strix]: learned per-expert codebooks).
  *   Activations: per 32-block, optional H32 (Sylvester FWHT, butterflies
- *   h = 1..16, then * fp32(1/sqrt(32))), d = amax/127, q = clamp(rint(v/d)).
+ *   h = 1..16, then * fp32(1/sqrt(32))), d = amax/127 (zero or subnormal d:
+ *   block stored as zero), q = clamp(rint(v * (1/d)), -127, 127).
  *
  * Conventions:
  *   - Every pointer argument of a launch entry point is a DEVICE pointer unless

@@ -9,7 +9,8 @@ multiply-add):
 1. optional H32: v <- FWHT32(v), then v_i <- v_i * c, c = fp32 nearest 1/sqrt(32);
 2. amax = max |v_i|;
 3. d = amax / 127;
-4. id = 1 / d if d != 0 else 0;
+4. if d < 2^-126 (zero or subnormal, where 1/d would overflow) the block is
+   stored as d = 0, q = 0; otherwise id = 1 / d;
 5. q_i = clamp(rint(v_i * id), -127, 127), rint = round half to even.
 """
 from __future__ import annotations
@@ -38,9 +39,10 @@ def quantize_act(x: np.ndarray, rot: int = 0):
         v = (v * INV_SQRT32).astype(np.float32)
     amax = np.max(np.abs(v), axis=-1)                              # exact
     d = (amax / np.float32(127.0)).astype(np.float32)              # IEEE division
-    with np.errstate(divide="ignore"):
-        inv = np.where(d != 0, np.float32(1.0) / np.where(d != 0, d, np.float32(1.0)),
-                       np.float32(0.0)).astype(np.float32)
+    normal = d >= np.float32(2.0 ** -126)
+    d = np.where(normal, d, np.float32(0.0)).astype(np.float32)
+    inv = np.where(normal, np.float32(1.0) / np.where(normal, d, np.float32(1.0)),
+                   np.float32(0.0)).astype(np.float32)
     t = (v * inv[..., None]).astype(np.float32)                    # fp32 product
     q = np.clip(np.rint(t), -127, 127).astype(np.int8)             # half to even
     return q.reshape(x.shape), d

@@ -46,6 +46,10 @@ def test_quant_act_bit_exact(rot):
     x[0, :32] = 0.0                                         # zero block
     x[1, :32] = np.arange(32) - 15.5                       # halves: ties to even
     x[2, 32:64] = 127.0 * (np.arange(32) % 3 - 1)          # exact multiples
+    x[3, :32] = np.float32(1e-38) * (np.arange(32) - 16)    # subnormal scale -> zero block
+    x[4, :32] = 0.0
+    x[4, 0] = np.float32(127 * 2.0 ** -126)                 # scale exactly 2^-126
+    x[4, 1] = np.float32(-0.5 * 127 * 2.0 ** -126)
     xq_ref, dx_ref = quant.quantize_act(x, rot)
     xd = dev(x)
     xq = torch.empty((7, 768), dtype=torch.int8, device="cuda")

@@ -84,6 +84,19 @@ def test_hand_worked_blocks():
     assert np.all(d == 0) and np.all(q == 0)
 
 
+def test_underflowing_block_is_zero():
+    """A block whose scale amax/127 is zero or subnormal is stored as zero
+    (1/d would overflow); a block whose scale is exactly 2^-126 is kept."""
+    v = np.zeros(64, np.float32)
+    v[:32] = np.float32(1e-38) * (np.arange(32) - 16)
+    v[32] = np.float32(127 * 2.0 ** -126)
+    v[33] = np.float32(-0.5 * 127 * 2.0 ** -126)
+    q, d = quant.quantize_act(v)
+    assert d[0] == 0 and np.all(q[:32] == 0)
+    assert d[1] == np.float32(2.0 ** -126)
+    assert q[32] == 127 and q[33] == -64                   # -63.5 -> -64 (half to even)
+
+
 def test_scale_steps_exact_rational():
     """d and 1/d are the correctly rounded binary32 values, checked with exact
     rationals on the binary32 grid around them."""
