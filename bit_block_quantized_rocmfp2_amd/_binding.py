@@ -81,6 +81,8 @@ def _load():
         "qmoe_quant_act": (c_int, [c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
         "qmoe_block_dots": (c_int, [c_int, c_int64, c_int64, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p,
                                     c_void_p]),
+        "qmoe_timing_enable": (c_int, [c_int]),
+        "qmoe_timing_read": (c_int, [c_char_p, POINTER(c_double), POINTER(c_int)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -95,7 +97,7 @@ EXPORTED = (
     "qmoe_strerror", "qmoe_last_error", "qmoe_version", "qmoe_block_bytes", "qmoe_packed_bytes", "qmoe_pack",
     "qmoe_unpack", "qmoe_layer_check", "qmoe_workspace_bytes", "qmoe_workspace_layout", "qmoe_route",
     "qmoe_decode_layer", "qmoe_prefill_layer", "qmoe_matvec_workspace_bytes", "qmoe_matvec", "qmoe_quant_act",
-    "qmoe_block_dots",
+    "qmoe_block_dots", "qmoe_timing_enable", "qmoe_timing_read",
 )
 
 
@@ -225,3 +227,15 @@ def qmoe_quant_act(x, rot, xq, dx, stream=None) -> None:
 def qmoe_block_dots(fmt, rows, k, w, cb, xq, P, stream=None) -> None:
     _check(LIB.qmoe_block_dots(fmt, rows, k, _ptr(w), _nbytes(w), _ptr(cb), _ptr(xq), _ptr(P), _stream(stream)),
            "qmoe_block_dots")
+
+
+def qmoe_timing_enable(on: bool) -> None:
+    _check(LIB.qmoe_timing_enable(1 if on else 0), "qmoe_timing_enable")
+
+
+def qmoe_timing_read(name: str):
+    """-> (total_ms, count) of the recorded launches of kernel ``name``."""
+    ms = c_double()
+    n = c_int()
+    _check(LIB.qmoe_timing_read(name.encode(), ctypes.byref(ms), ctypes.byref(n)), "qmoe_timing_read")
+    return ms.value, n.value

@@ -12,7 +12,8 @@ using namespace qmoe;
 
 namespace {
 
-constexpr int kMaxExperts = 1024;
+constexpr int kMaxExperts = 512;
+constexpr int kMaxHidden = 8192;
 constexpr int kMaxTopk = 8;
 constexpr size_t kAlign = 256;
 
@@ -55,6 +56,7 @@ extern "C" int qmoe_layer_check(const qmoe_layer* L) {
   if (L->fmt_gate != L->fmt_up)
     QMOE_FAIL(QMOE_E_FORMAT, "gate format FP%d differs from up format FP%d (must match)", L->fmt_gate, L->fmt_up);
   if (L->hidden % 32 || L->inter % 32) QMOE_FAIL(QMOE_E_SHAPE, "hidden=%d / inter=%d not multiples of 32", L->hidden, L->inter);
+  if (L->hidden > kMaxHidden) QMOE_FAIL(QMOE_E_SHAPE, "hidden=%d exceeds %d", L->hidden, kMaxHidden);
   if (!L->w_router) QMOE_FAIL(QMOE_E_INVAL, "router: missing weights (NULL)");
   const size_t rneed = (size_t)L->n_experts * L->hidden * 2;
   if (L->w_router_bytes < rneed) QMOE_FAIL(QMOE_E_SIZE, "router: %zu bytes < %zu required", L->w_router_bytes, rneed);

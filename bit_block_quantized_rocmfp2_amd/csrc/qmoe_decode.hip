@@ -1,0 +1,439 @@
+// Decode layer (gfx950): the top-k SwiGLU MoE layer for q = 1..4 tokens in three
+// stream-ordered launches, with no host synchronisation.
+//
+// Page citations:
+//   [Strix-284B] lucebox.com, "DeepSeek V4 Flash: 284B model, up to 32 tok/s on
+//     AMD Ryzen AI MAX+ 395": section "ROCmFPX: fitting 284B weights into 128 GB"
+//     (decode streams the active expert weights, so it is bound by memory
+//     traffic; packed blocks are expanded in registers and fed to integer dot
+//     products) and section "Decode: up to 32 tok/s" (q = 4 verification
+//     columns; each packed weight is decoded once and applied to all columns;
+//     dedicated top-k routing kernels).
+//   [0731-Strix] lucebox.com, "Lucebox × Geometric: DeepSeek V4 Flash 0731
+//     reaches 32.7 tok/s on AMD Strix Halo", section "Lucebox Engine integration
+//     with Geometric" (a sync-free MoE decode path) and section "How the model
+//     fits on AMD Strix Halo" (gate/up 2.5 bpw, down 3.5 bpw, per-expert
+//     codebooks).
+//
+//   k_route    one wave per expert: fp64 logits of the q tokens; every workgroup
+//              also quantizes a share of the tokens to int8 per 32-block. The
+//              last workgroup to finish (one counter increment each, no waiting)
+//              selects the top-k of every token and writes the plan: the union
+//              of the chosen experts in ascending id, a column mask and the
+//              routing weights per expert.
+//   k_gateup   one workgroup per (planned expert, 32 rows): the gate and up rows
+//              are streamed once (all loads of a wave issued before the first
+//              use), each block expanded once for every column routed to the
+//              expert; SwiGLU, then requantization of the 32-row block (+ H32)
+//              for the down projection. Workgroups beyond the plan exit.
+//   k_down     one workgroup per group of rows: the rows of every planned expert
+//              (loads issued together), per column contributions accumulated
+//              per lane in ascending expert id with the routing weights,
+//              reduced once.
+// Kernel boundaries make each launch's results visible to the next across the
+// 8 XCDs (separate L2 caches); inside k_route the logits of the other
+// workgroups are written and read with agent-scope atomics, so no cache-wide
+// fence is needed.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "qmoe_device.h"
+#include "qmoe_host.h"
+#include "qmoe_internal.h"
+
+using namespace qk;
+using namespace qmoe;
+
+namespace {
+
+struct DecodeArgs {
+  const uint16_t* w_router;
+  const double* bias;
+  const uint8_t* gate;
+  const uint8_t* up;
+  const uint8_t* down;
+  const int8_t* cb_gate;
+  const int8_t* cb_up;
+  const int8_t* cb_down;
+  const float* x;
+  float* out;
+  uint32_t* ctrl;
+  int8_t* xq;
+  float* dx;
+  double* logits;
+  int32_t* idx;
+  float* gw;
+  int32_t* plan;
+  int8_t* hq;
+  float* dh;
+  size_t gu_row_bytes, gu_stride, dn_row_bytes, dn_stride;
+  int hidden, inter, E, K, q, rot_gateup, rot_down;
+  int nb_h, nb_i;
+  int dn_lpr_log2;
+  int n_router, quant_per_wg;
+};
+
+// ------------------------------------------------------------ k_route
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+template <int Q>
+__global__ __launch_bounds__(256) void k_route(DecodeArgs a) {
+  __shared__ int s_last;
+  __shared__ int s_ids[4][8];
+  __shared__ float s_w[4][8];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // 1. logits of 4 experts (one per wave), published with agent-scope atomics
+  const int e = blockIdx.x * 4 + wave;
+  if (e < a.E) {
+    double lg[Q];
+    router_wave<Q>(a.w_router, a.x, a.q, a.hidden, a.bias, e, 0, lane, lg);
+    double mine = lg[0];   // lane t publishes token t
+#pragma unroll
+    for (int t = 1; t < Q; ++t)
+      if (lane == t) mine = lg[t];
+    if (lane < a.q)
+      (void)__hip_atomic_exchange(reinterpret_cast<unsigned long long*>(a.logits) + (size_t)lane * a.E + e,
+                                  (unsigned long long)__double_as_longlong(mine), __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // 2. this workgroup's share of the int8 token quantization (read by the next launches)
+  const int nblk = a.q * a.nb_h;
+  const int b_end = min((int)(blockIdx.x + 1) * a.quant_per_wg, nblk);
+  for (int b = blockIdx.x * a.quant_per_wg + tid; b < b_end; b += blockDim.x) {
+    float v[32];
+    const float4* src = reinterpret_cast<const float4*>(a.x + (size_t)b * 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float4 f = src[i];
+      v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+    uint32_t qv[8];
+    float d;
+    quant_block32(v, a.rot_gateup, qv, &d);
+    uint4* dst = reinterpret_cast<uint4*>(a.xq + (size_t)b * 32);
+    dst[0] = make_uint4(qv[0], qv[1], qv[2], qv[3]);
+    dst[1] = make_uint4(qv[4], qv[5], qv[6], qv[7]);
+    a.dx[b] = d;
+  }
+  // 3. the last workgroup to get here does the top-k and the plan
+  wait_vmem();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kCtrlRouterDone], 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (done == (uint32_t)a.n_router - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  if (wave < a.q) {
+    int sel[8];
+    float g[8];
+    topk_wave<true>(a.logits + (size_t)wave * a.E, a.E, a.K, lane, sel, g);
+    if (lane < a.K) {
+      int sv = sel[0];
+      float gv = g[0];
+#pragma unroll
+      for (int k = 1; k < 8; ++k)
+        if (lane == k) {
+          sv = sel[k];
+          gv = g[k];
+        }
+      a.idx[wave * a.K + lane] = sv;
+      a.gw[wave * a.K + lane] = gv;
+      s_ids[wave][lane] = sv;
+      s_w[wave][lane] = gv;
+    }
+  }
+  __syncthreads();
+  // Plan, in wave 0: one (token, expert) candidate per lane. A candidate is the
+  // first of its expert id if no lower lane holds the same id; its plan slot is
+  // the number of distinct ids smaller than its own.
+  if (wave == 0) {
+    const int n = a.q * a.K;
+    const bool have = lane < n;
+    const int t = have ? lane / a.K : 0;
+    const int k = have ? lane - t * a.K : 0;
+    const int ex = have ? s_ids[t][k] : 0x7FFFFFFF;
+    bool first = have;
+    uint32_t mask = 0;
+    float w4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < n; ++j) {
+      const int tj = j / a.K, kj = j - tj * a.K;
+      if (s_ids[tj][kj] == ex) {
+        mask |= 1u << tj;
+        const float wj = s_w[tj][kj];
+        if (tj == 0) w4[0] = wj;
+        if (tj == 1) w4[1] = wj;
+        if (tj == 2) w4[2] = wj;
+        if (tj == 3) w4[3] = wj;
+        if (j < lane) first = false;
+      }
+    }
+    const uint64_t firsts = __ballot(first);
+    int slot = 0;
+    for (int j = 0; j < n; ++j) {
+      const int tj = j / a.K;
+      if (((firsts >> j) & 1ull) && s_ids[tj][j - tj * a.K] < ex) ++slot;
+    }
+    const int U = __popcll(firsts);
+    if (lane < kPlanMax && lane >= U) {        // unused slots
+      a.plan[kPlanIdOff + lane] = -1;
+      a.plan[kPlanMaskOff + lane] = 0;
+    }
+    if (first) {
+      a.plan[kPlanIdOff + slot] = ex;
+      a.plan[kPlanMaskOff + slot] = (int)mask;
+      float* pw = reinterpret_cast<float*>(a.plan + kPlanWOff) + 4 * slot;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) pw[c] = w4[c];
+    }
+    if (lane == 0) {
+      a.plan[0] = U;
+      a.ctrl[kCtrlRouterDone] = 0;             // ready for the next call
+    }
+  }
+}
+
+// ------------------------------------------------------------ k_gateup
+// 8 waves; wave w owns rows 4w..4w+3 of both gate and up of the workgroup's 32
+// rows. Lanes cover NBL consecutive blocks each.
+template <int FMT, int Q>
+__global__ __launch_bounds__(512) void k_gateup(DecodeArgs a) {
+  constexpr int NBL = (FMT == 4) ? 1 : 2;
+  constexpr int RPW = 4;
+  __shared__ float s_a[4][32];
+  const int u = blockIdx.y, rb = blockIdx.x;
+  const int U = a.plan[0];
+  if (u >= U) return;
+  const int e = a.plan[kPlanIdOff + u];
+  const uint32_t mask = (uint32_t)a.plan[kPlanMaskOff + u];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row0 = rb * 32 + wave * RPW;
+  const uint8_t* gbase = a.gate + (size_t)e * a.gu_stride;
+  const uint8_t* ubase = a.up + (size_t)e * a.gu_stride;
+  uint32_t cbg[4], cbu[4];
+  load_codebook<FMT>(a.cb_gate + ((size_t)e << FMT), cbg);
+  load_codebook<FMT>(a.cb_up + ((size_t)e << FMT), cbu);
+  const int nb = a.nb_h;
+  float ag[RPW][Q], au[RPW][Q];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int t = 0; t < Q; ++t) ag[r][t] = au[r][t] = 0.0f;
+  for (int c0 = 0; c0 < nb; c0 += 64 * NBL) {
+    const int b = c0 + lane * NBL;
+    if (b < nb) {
+      Blocks<FMT, NBL> bg[RPW], bu[RPW];
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        bg[r].load(gbase + (size_t)(row0 + r) * a.gu_row_bytes, nb, b);
+        bu[r].load(ubase + (size_t)(row0 + r) * a.gu_row_bytes, nb, b);
+      }
+      Acts<NBL> act[Q];
+#pragma unroll
+      for (int t = 0; t < Q; ++t)
+        if (mask >> t & 1) act[t].load(a.xq + (size_t)t * nb * 32, a.dx + (size_t)t * nb, b);
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int i = 0; i < NBL; ++i) {
+          uint32_t wg[8], wu[8];
+          bg[r].expand(i, cbg, wg);
+          bu[r].expand(i, cbu, wu);
+          const float sg = bg[r].scale(i), su = bu[r].scale(i);
+#pragma unroll
+          for (int t = 0; t < Q; ++t)
+            if (mask >> t & 1) {
+              const int pg = block_dot(wg, act[t].q[i]);
+              const int pu = block_dot(wu, act[t].q[i]);
+              ag[r][t] = fmaf((float)pg, sg * act[t].d[i], ag[r][t]);
+              au[r][t] = fmaf((float)pu, su * act[t].d[i], au[r][t]);
+            }
+        }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int t = 0; t < Q; ++t)
+      if (mask >> t & 1) {
+        const float gv = group_sum(ag[r][t], 64);
+        const float uv = group_sum(au[r][t], 64);
+        if (lane == 0) s_a[t][wave * RPW + r] = gv / (1.0f + expf(-gv)) * uv;
+      }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < Q && (mask >> t & 1)) {
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v[j] = s_a[t][j];
+    uint32_t qv[8];
+    float d;
+    quant_block32(v, a.rot_down, qv, &d);
+    const size_t slot = (size_t)u * 4 + t;
+    uint4* dst = reinterpret_cast<uint4*>(a.hq + slot * a.inter + (size_t)rb * 32);
+    dst[0] = make_uint4(qv[0], qv[1], qv[2], qv[3]);
+    dst[1] = make_uint4(qv[4], qv[5], qv[6], qv[7]);
+    a.dh[slot * a.nb_i + rb] = d;
+  }
+}
+
+// ------------------------------------------------------------ k_down
+// Each wave handles 64/LPR rows (LPR lanes per row, NBL blocks per lane); the
+// row chunks of UB planned experts are loaded together before any is used.
+template <int FMT, int Q>
+__global__ __launch_bounds__(256) void k_down(DecodeArgs a) {
+  constexpr int NBL = (FMT == 4) ? 1 : 2;
+  constexpr int UB = (Q == 1) ? 6 : ((Q == 2) ? 4 : 3);
+  const int lpr_log2 = a.dn_lpr_log2;
+  const int lpr = 1 << lpr_log2;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sub = lane >> lpr_log2, sl = lane & (lpr - 1);
+  const int row = (blockIdx.x * 4 + wave) * (64 >> lpr_log2) + sub;
+  const bool row_ok = row < a.hidden;
+  const int U = a.plan[0];
+  const float* pw = reinterpret_cast<const float*>(a.plan + kPlanWOff);
+  const int nb = a.nb_i;
+  float acc[Q];
+#pragma unroll
+  for (int t = 0; t < Q; ++t) acc[t] = 0.0f;
+  for (int c0 = 0; c0 < nb; c0 += lpr * NBL) {
+    const int b = c0 + sl * NBL;
+    const bool ok = row_ok && b < nb;
+    for (int u0 = 0; u0 < U; u0 += UB) {
+      Blocks<FMT, NBL> bl[UB];
+      int ej[UB];
+#pragma unroll
+      for (int j = 0; j < UB; ++j) {
+        ej[j] = (u0 + j < U) ? a.plan[kPlanIdOff + u0 + j] : 0;
+        if (ok && u0 + j < U) bl[j].load(a.down + (size_t)ej[j] * a.dn_stride + (size_t)row * a.dn_row_bytes, nb, b);
+      }
+#pragma unroll
+      for (int j = 0; j < UB; ++j) {
+        const int u = u0 + j;
+        if (u < U) {
+          const uint32_t mask = (uint32_t)a.plan[kPlanMaskOff + u];
+          uint32_t cb[4];
+          load_codebook<FMT>(a.cb_down + ((size_t)ej[j] << FMT), cb);
+          if (ok) {
+#pragma unroll
+            for (int t = 0; t < Q; ++t)
+              if (mask >> t & 1) {
+                const float wgt = pw[4 * u + t];
+                const size_t slot = (size_t)u * 4 + t;
+                Acts<NBL> act;
+                act.load(a.hq + slot * a.inter, a.dh + slot * nb, b);
+#pragma unroll
+                for (int i = 0; i < NBL; ++i) {
+                  uint32_t w[8];
+                  bl[j].expand(i, cb, w);
+                  const int p = block_dot(w, act.q[i]);
+                  acc[t] = fmaf((float)p, bl[j].scale(i) * act.d[i] * wgt, acc[t]);
+                }
+              }
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < Q; ++t) {
+    const float v = group_sum(acc[t], lpr);
+    if (sl == 0 && row_ok) a.out[(size_t)t * a.hidden + row] = v;
+  }
+}
+
+template <int FG, int FD, int Q>
+int launch_decode_t(const DecodeArgs& a, int U_max, hipStream_t s) {
+  {
+    KernelTimer kt("route", s);
+    hipLaunchKernelGGL(k_route<Q>, dim3(a.n_router), dim3(256), 0, s, a);
+  }
+  int st = launch_check("route");
+  if (st) return st;
+  {
+    KernelTimer kt("gateup", s);
+    hipLaunchKernelGGL((k_gateup<FG, Q>), dim3(a.inter / 32, U_max), dim3(512), 0, s, a);
+  }
+  if ((st = launch_check("gateup"))) return st;
+  const int rows_per_wg = 4 * (64 >> a.dn_lpr_log2);
+  {
+    KernelTimer kt("down", s);
+    hipLaunchKernelGGL((k_down<FD, Q>), dim3((a.hidden + rows_per_wg - 1) / rows_per_wg), dim3(256), 0, s, a);
+  }
+  return launch_check("down");
+}
+
+template <int Q>
+int launch_decode_q(const DecodeArgs& a, int U_max, int fg, int fd, hipStream_t s) {
+  if (fg == 2 && fd == 3) return launch_decode_t<2, 3, Q>(a, U_max, s);
+  if (fg == 2 && fd == 2) return launch_decode_t<2, 2, Q>(a, U_max, s);
+  if (fg == 2 && fd == 4) return launch_decode_t<2, 4, Q>(a, U_max, s);
+  if (fg == 3 && fd == 3) return launch_decode_t<3, 3, Q>(a, U_max, s);
+  if (fg == 3 && fd == 2) return launch_decode_t<3, 2, Q>(a, U_max, s);
+  if (fg == 3 && fd == 4) return launch_decode_t<3, 4, Q>(a, U_max, s);
+  if (fg == 4 && fd == 3) return launch_decode_t<4, 3, Q>(a, U_max, s);
+  if (fg == 4 && fd == 2) return launch_decode_t<4, 2, Q>(a, U_max, s);
+  return launch_decode_t<4, 4, Q>(a, U_max, s);
+}
+
+}  // namespace
+
+extern "C" int qmoe_decode_layer(const qmoe_layer* L, const float* x, int32_t q, float* out, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  clear_error();
+  if (q < 1 || q > 4) QMOE_FAIL(QMOE_E_SHAPE, "q=%d outside 1..4", q);
+  WsPtrs w;
+  int st = ws_ptrs(L, q, ws, ws_bytes, &w);
+  if (st) return st;
+  if (!x || !out) QMOE_FAIL(QMOE_E_INVAL, "NULL pointer");
+  if (!aligned16(x)) QMOE_FAIL(QMOE_E_INVAL, "x not 16-byte aligned");
+  FormatInfo fg, fd;
+  format_info(L->fmt_gate, &fg);
+  format_info(L->fmt_down, &fd);
+  DecodeArgs a{};
+  a.w_router = L->w_router;
+  a.bias = L->router_bias;
+  a.gate = static_cast<const uint8_t*>(L->gate);
+  a.up = static_cast<const uint8_t*>(L->up);
+  a.down = static_cast<const uint8_t*>(L->down);
+  a.cb_gate = L->cb_gate;
+  a.cb_up = L->cb_up;
+  a.cb_down = L->cb_down;
+  a.x = x;
+  a.out = out;
+  a.ctrl = w.ctrl;
+  a.xq = w.xq;
+  a.dx = w.dx;
+  a.logits = w.logits;
+  a.idx = w.idx;
+  a.gw = w.gw;
+  a.plan = w.plan;
+  a.hq = w.hq;
+  a.dh = w.dh;
+  a.hidden = L->hidden;
+  a.inter = L->inter;
+  a.E = L->n_experts;
+  a.K = L->topk;
+  a.q = q;
+  a.rot_gateup = L->rot_gateup;
+  a.rot_down = L->rot_down;
+  a.nb_h = L->hidden / 32;
+  a.nb_i = L->inter / 32;
+  a.gu_row_bytes = (size_t)a.nb_h * fg.block_bytes;
+  a.gu_stride = a.gu_row_bytes * L->inter;
+  a.dn_row_bytes = (size_t)a.nb_i * fd.block_bytes;
+  a.dn_stride = a.dn_row_bytes * L->hidden;
+  a.dn_lpr_log2 = ilog2(lanes_per_row(a.nb_i, L->fmt_down == QMOE_FP4 ? 1 : 2));
+  a.n_router = (L->n_experts + 3) / 4;
+  a.quant_per_wg = (q * a.nb_h + a.n_router - 1) / a.n_router;
+  const int U_max = std::min(q * L->topk, L->n_experts);
+  hipStream_t s = as_stream(stream);
+  switch (q) {
+    case 1: return launch_decode_q<1>(a, U_max, L->fmt_gate, L->fmt_down, s);
+    case 2: return launch_decode_q<2>(a, U_max, L->fmt_gate, L->fmt_down, s);
+    case 3: return launch_decode_q<3>(a, U_max, L->fmt_gate, L->fmt_down, s);
+    default: return launch_decode_q<4>(a, U_max, L->fmt_gate, L->fmt_down, s);
+  }
+}

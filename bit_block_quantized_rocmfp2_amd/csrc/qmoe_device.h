@@ -57,11 +57,13 @@ __device__ __forceinline__ void load_codebook(const int8_t* cb, uint32_t w[4]) {
 }
 
 // NBL consecutive blocks of one row, starting at block b (row-planar layout).
+// load() only issues the loads (raw scale bits are kept), so that a caller can
+// put the loads of many rows in flight before touching any of them.
 template <int FMT, int NBL>
 struct Blocks {
   uint32_t lo[NBL][Fmt<FMT>::kLoWords];
   uint32_t hi[NBL];
-  float s[NBL];
+  uint32_t sraw;   // NBL fp16 scales (2 bytes each) or NBL E8M0 bytes
 
   __device__ __forceinline__ void load(const uint8_t* row, int nb, int b) {
     constexpr int LW = Fmt<FMT>::kLoWords;
@@ -95,22 +97,23 @@ struct Blocks {
     }
     const uint8_t* sc = after_lo + (size_t)nb * 4 * Fmt<FMT>::kHi;
     if constexpr (Fmt<FMT>::kScaleBytes == 2) {
-      if constexpr (NBL == 2) {
-        uint32_t w = *reinterpret_cast<const uint32_t*>(sc + (size_t)b * 2);
-        s[0] = half_bits_to_float(w & 0xFFFFu);
-        s[NBL - 1] = half_bits_to_float(w >> 16);
-      } else {
-        s[0] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(sc + (size_t)b * 2));
-      }
+      if constexpr (NBL == 2)
+        sraw = *reinterpret_cast<const uint32_t*>(sc + (size_t)b * 2);
+      else
+        sraw = *reinterpret_cast<const uint16_t*>(sc + (size_t)b * 2);
     } else {
-      if constexpr (NBL == 2) {
-        uint32_t w = *reinterpret_cast<const uint16_t*>(sc + b);
-        s[0] = e8m0_to_float(w & 0xFFu);
-        s[NBL - 1] = e8m0_to_float(w >> 8);
-      } else {
-        s[0] = e8m0_to_float(sc[b]);
-      }
+      if constexpr (NBL == 2)
+        sraw = *reinterpret_cast<const uint16_t*>(sc + b);
+      else
+        sraw = sc[b];
     }
+  }
+
+  __device__ __forceinline__ float scale(int i) const {
+    if constexpr (Fmt<FMT>::kScaleBytes == 2)
+      return half_bits_to_float((sraw >> (16 * i)) & 0xFFFFu);
+    else
+      return e8m0_to_float((sraw >> (8 * i)) & 0xFFu);
   }
 
   // Expand block i into 8 dwords of int8 weights; out[g] covers weights 4g..4g+3.
@@ -217,6 +220,164 @@ __device__ __forceinline__ void quant_block32(float v[32], int rot, uint32_t q[8
     q[g] = w;
   }
   *d_out = d;
+}
+
+
+// ---------------------------------------------------------------------------
+// Router: one wave computes the fp64 logits of expert e for tokens t0..t0+TT-1.
+// Lane l holds blocks l + 64c. Per block: sequential fp64 sum of the 32 exact
+// products (fp16 x fp32 is exact in fp64, so fma == mul + add); then the
+// stride-halving tree: in-lane stages (strides >= 64 blocks) followed by
+// xor-butterfly stages m = 32..1 across lanes, each only when m < P2 (lane j +
+// lane j^m equals s_j + s_{j+m} for j < m). Routing: 256 experts, 6 routed
+// (lucebox.com, "Lucebox × Geometric: DeepSeek V4 Flash 0731 reaches 32.7
+// tok/s on AMD Strix Halo", section "Run with Lucebox Engine").
+constexpr int kRouterMaxC = 2;   // hidden <= 32 * 64 * 2 = 8192
+
+// On return every lane holds the logits of tokens t0..t0+TT-1 in out[] (bias
+// included; entries for tokens >= ntok are undefined).
+template <int TT>
+__device__ __forceinline__ void router_wave(const uint16_t* __restrict__ W, const float* __restrict__ x, int ntok,
+                                            int H, const double* __restrict__ bias, int e, int t0, int lane,
+                                            double out[TT]) {
+  const int nb = H >> 5;
+  int P2 = 1;
+  while (P2 < nb) P2 <<= 1;
+  const int C = P2 > 64 ? P2 / 64 : 1;
+  double s[TT][kRouterMaxC];
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int c = 0; c < kRouterMaxC; ++c) s[t][c] = 0.0;
+#pragma unroll
+  for (int c = 0; c < kRouterMaxC; ++c) {
+    const int b = lane + 64 * c;
+    if (c < C && b < nb) {
+      const uint4* wp = reinterpret_cast<const uint4*>(W + (size_t)e * H + (size_t)b * 32);
+      uint32_t wv[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint4 u = wp[i];
+        wv[4 * i] = u.x; wv[4 * i + 1] = u.y; wv[4 * i + 2] = u.z; wv[4 * i + 3] = u.w;
+      }
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        if (t0 + t < ntok) {
+          const float4* xp = reinterpret_cast<const float4*>(x + (size_t)(t0 + t) * H + (size_t)b * 32);
+          double acc = 0.0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            float4 f = xp[i];
+            const float xs[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int j = 4 * i + k;
+              const uint32_t hb = (j & 1) ? (wv[j >> 1] >> 16) : (wv[j >> 1] & 0xFFFFu);
+              acc = fma((double)half_bits_to_float(hb), (double)xs[k], acc);
+            }
+          }
+          s[t][c] = acc;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+#pragma unroll
+    for (int n = kRouterMaxC / 2; n >= 1; n >>= 1)
+      if (n < C)
+#pragma unroll
+        for (int c = 0; c < n; ++c) s[t][c] = s[t][c] + s[t][c + n];
+    double v = s[t][0];
+    for (int m = 32; m >= 1; m >>= 1)
+      if (m < P2) v = v + __shfl_xor(v, m);
+    out[t] = bias ? v + bias[e] : v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top-k of one token's E logits (one wave, K <= 8, E <= 512). Equal logits go
+// to the lower id. Every lane ends with the selected ids in ascending order in
+// sel[0..K) (unused entries 0x7FFFFFFF) and the softmax over the selected
+// logits (fp64, max subtracted, summed in ascending id order) in g[0..K).
+constexpr int kTopkMaxPerLane = 8;   // E <= 512
+
+__device__ __forceinline__ bool topk_better(double av, int ai, double bv, int bi) {
+  return av > bv || (av == bv && ai < bi);
+}
+
+// COHERENT = true reads the logits with agent-scope atomic loads (they were
+// written by other workgroups of the same launch).
+template <bool COHERENT = false>
+__device__ __forceinline__ void topk_wave(const double* __restrict__ row, int E, int K, int lane, int sel[8],
+                                          float g[8]) {
+  double v[kTopkMaxPerLane];
+#pragma unroll
+  for (int j = 0; j < kTopkMaxPerLane; ++j) {
+    const int e = lane + 64 * j;
+    if (e < E) {
+      if constexpr (COHERENT)
+        v[j] = __longlong_as_double((long long)__hip_atomic_load(reinterpret_cast<const uint64_t*>(row) + e,
+                                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      else
+        v[j] = row[e];
+    } else {
+      v[j] = -INFINITY;
+    }
+  }
+  uint32_t taken = 0;
+  double sv[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    sel[k] = 0x7FFFFFFF;
+    sv[k] = -INFINITY;
+    if (k < K) {
+      double bv = -INFINITY;
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int j = 0; j < kTopkMaxPerLane; ++j) {
+        const int e = lane + 64 * j;
+        if (e < E && !((taken >> j) & 1u) && topk_better(v[j], e, bv, bi)) {
+          bv = v[j];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const double ov = __shfl_xor(bv, m);
+        const int oi = __shfl_xor(bi, m);
+        if (topk_better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      sel[k] = bi;
+      sv[k] = bv;
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    }
+  }
+  const double m = sv[0];                      // the first pick is the largest logit
+  // ascending ids: odd-even transposition sort of the 8 (id, logit) pairs
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int i = r & 1; i < 7; i += 2)
+      if (sel[i] > sel[i + 1]) {
+        const int ti = sel[i];
+        sel[i] = sel[i + 1];
+        sel[i + 1] = ti;
+        const double tv = sv[i];
+        sv[i] = sv[i + 1];
+        sv[i + 1] = tv;
+      }
+  double ex[8], S = 0.0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    ex[k] = (k < K) ? exp(sv[k] - m) : 0.0;
+    if (k < K) S = S + ex[k];
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) g[k] = (k < K) ? (float)(ex[k] / S) : 0.0f;
 }
 
 }  // namespace qk

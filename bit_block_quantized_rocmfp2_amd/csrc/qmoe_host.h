@@ -1,0 +1,87 @@
+// Host-side helpers shared by the HIP translation units of libqmoe.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "qmoe_internal.h"
+
+namespace qmoe {
+
+// Layer workspace control words (uint32, in the `ctrl` region). Each counter has
+// a 256-byte line of its own so that polling one does not queue behind traffic
+// to another.
+enum CtrlWord : int {
+  kCtrlError = 0,          // sticky device error flags (bit 0: a bounded wait timed out)
+  kCtrlTicket = 64,        // next task ticket of the persistent decode kernel
+  kCtrlRouterDone = 128,   // router tasks finished
+  kCtrlPlanReady = 192,    // top-k and expert plan published
+  kCtrlGateUpDone = 256,   // gate/up tasks finished
+  kCtrlExit = 320,         // workgroups that left the task loop
+};
+
+// Decode plan (int32 words in the `plan` region): [0] U distinct experts,
+// [1..32] expert ids ascending, [33..64] column masks, fp32 weights from word
+// 128: w[u][t] for u < 32, t < 4.
+constexpr int kPlanMax = 32;
+constexpr int kPlanIdOff = 1;
+constexpr int kPlanMaskOff = 1 + kPlanMax;
+constexpr int kPlanWOff = 128;
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int launch_check(const char* what);
+
+inline int ilog2(int v) {
+  int l = 0;
+  while ((1 << (l + 1)) <= v) ++l;
+  return l;
+}
+
+// Lanes per row for a row of nb blocks processed nbl at a time: the largest power
+// of two <= nb/nbl, at most 64 and at least 1.
+inline int lanes_per_row(int nb, int nbl) {
+  int chunks = (nb + nbl - 1) / nbl;
+  int l = 1;
+  while (l * 2 <= chunks && l < 64) l *= 2;
+  return l;
+}
+
+struct WsPtrs {
+  uint32_t* ctrl;
+  int8_t* xq;
+  float* dx;
+  int32_t* idx;
+  float* gw;
+  double* logits;
+  int32_t* plan;
+  int8_t* hq;
+  float* dh;
+  uint8_t* group;
+  float* ypair;
+};
+
+int ws_ptrs(const qmoe_layer* L, int32_t ntok, void* ws, size_t ws_bytes, WsPtrs* p);
+
+// Opt-in kernel timing: brackets the kernel launched in its scope with two HIP
+// events on the launch stream (see qmoe_timing_enable / qmoe_timing_read).
+class KernelTimer {
+ public:
+  KernelTimer(const char* name, hipStream_t s);
+  ~KernelTimer();
+
+ private:
+  int slot_ = -1;
+  hipStream_t s_;
+};
+
+// Number of compute units of the current device, cached.
+int device_cu_count();
+
+// Launch helpers shared by the entry points (qmoe_kernels.hip).
+int launch_quant(const float* x, int64_t nblocks, int rot, int8_t* xq, float* dx, hipStream_t s);
+int launch_route(const qmoe_layer* L, const float* x, int32_t ntok, double* logits, int32_t* idx, float* gw,
+                 hipStream_t s);
+
+}  // namespace qmoe

@@ -55,7 +55,8 @@ extern "C" {
 typedef enum {
   QMOE_OK = 0,
   QMOE_E_INVAL = -1,     /* NULL pointer, bad enum value, bad flag            */
-  QMOE_E_SHAPE = -2,     /* K % 32 != 0, q not in 1..4, topk not in 1..min(E,8) */
+  QMOE_E_SHAPE = -2,     /* K % 32 != 0, q not in 1..4, topk not in 1..min(E,8),
+                            E > 512, hidden > 8192, rows not 16-byte multiples */
   QMOE_E_FORMAT = -3,    /* unknown format or unsupported format/rotation pair */
   QMOE_E_CODEBOOK = -4,  /* missing / truncated / mismatched codebook bytes     */
   QMOE_E_SCALE = -5,     /* non-finite fp16 scale or E8M0 0xFF (pack)           */
@@ -184,6 +185,15 @@ typedef struct {
 } qmoe_ws_layout;
 
 int qmoe_workspace_layout(const qmoe_layer* L, int32_t max_tokens, qmoe_ws_layout* out);
+
+/* Kernel timing (instrumentation). qmoe_timing_enable(1) starts recording, for
+ * every kernel that an entry point launches afterwards, a pair of HIP events on
+ * the call's stream; (0) stops; either call discards earlier records.
+ * qmoe_timing_read waits for the recorded kernels named `name` ("quant_act",
+ * "router", "topk", "gateup", "down", "matvec", "group", "gateup_mfma",
+ * "down_mfma", "combine") and returns their summed time in ms and their count. */
+int qmoe_timing_enable(int on);
+int qmoe_timing_read(const char* name, double* total_ms, int* count);
 
 #ifdef __cplusplus
 }
