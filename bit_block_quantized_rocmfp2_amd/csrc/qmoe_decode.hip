@@ -15,25 +15,25 @@
 //     fits on AMD Strix Halo" (gate/up 2.5 bpw, down 3.5 bpw, per-expert
 //     codebooks).
 //
-//   k_route    one wave per expert: fp64 logits of the q tokens; every workgroup
-//              also quantizes a share of the tokens to int8 per 32-block. The
-//              last workgroup to finish (one counter increment each, no waiting)
-//              selects the top-k of every token and writes the plan: the union
-//              of the chosen experts in ascending id, a column mask and the
-//              routing weights per expert.
-//   k_gateup   one workgroup per (planned expert, 32 rows): the gate and up rows
-//              are streamed once (all loads of a wave issued before the first
-//              use), each block expanded once for every column routed to the
-//              expert; SwiGLU, then requantization of the 32-row block (+ H32)
-//              for the down projection. Workgroups beyond the plan exit.
-//   k_down     one workgroup per group of rows: the rows of every planned expert
-//              (loads issued together), per column contributions accumulated
-//              per lane in ascending expert id with the routing weights,
-//              reduced once.
+//   k_route    one single-wave workgroup per expert: fp64 logits of the q
+//              tokens; the workgroups also share the int8 quantization of the
+//              tokens.
+//   k_gateup   one workgroup per (planned expert slot, 32 rows). Every
+//              workgroup first selects the top-k of each token from the logits
+//              and builds the plan itself (the union of the chosen experts in
+//              ascending id, a column mask and the routing weights per expert),
+//              so no workgroup waits for another; workgroup (0, 0) also writes
+//              the routing and the plan out. Then the gate and up rows are
+//              streamed once (all loads of a wave issued before the first use),
+//              each block expanded once for every column routed to the expert;
+//              SwiGLU, then requantization of the 32-row block (+ H32) for the
+//              down projection. Slots beyond the plan's size exit.
+//   k_down     one workgroup per group of rows: the plan is read in one round
+//              trip, the rows of every planned expert are loaded together, per
+//              column contributions are accumulated per lane in ascending
+//              expert id with the routing weights, and reduced once.
 // Kernel boundaries make each launch's results visible to the next across the
-// 8 XCDs (separate L2 caches); inside k_route the logits of the other
-// workgroups are written and read with agent-scope atomics, so no cache-wide
-// fence is needed.
+// 8 XCDs (separate L2 caches); no workgroup waits for another inside a launch.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -71,36 +71,25 @@ struct DecodeArgs {
   int hidden, inter, E, K, q, rot_gateup, rot_down;
   int nb_h, nb_i;
   int dn_lpr_log2;
-  int n_router, quant_per_wg;
+  int quant_per_wg;
 };
 
 // ------------------------------------------------------------ k_route
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
-
 template <int Q>
-__global__ __launch_bounds__(256) void k_route(DecodeArgs a) {
-  __shared__ int s_last;
-  __shared__ int s_ids[4][8];
-  __shared__ float s_w[4][8];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  // 1. logits of 4 experts (one per wave), published with agent-scope atomics
-  const int e = blockIdx.x * 4 + wave;
-  if (e < a.E) {
-    double lg[Q];
-    router_wave<Q>(a.w_router, a.x, a.q, a.hidden, a.bias, e, 0, lane, lg);
-    double mine = lg[0];   // lane t publishes token t
+__global__ __launch_bounds__(64) void k_route(DecodeArgs a) {
+  const int lane = threadIdx.x;
+  const int e = blockIdx.x;
+  double lg[Q];
+  router_wave<Q>(a.w_router, a.x, a.q, a.hidden, a.bias, e, 0, lane, lg);
+  double mine = lg[0];   // lane t writes token t
 #pragma unroll
-    for (int t = 1; t < Q; ++t)
-      if (lane == t) mine = lg[t];
-    if (lane < a.q)
-      (void)__hip_atomic_exchange(reinterpret_cast<unsigned long long*>(a.logits) + (size_t)lane * a.E + e,
-                                  (unsigned long long)__double_as_longlong(mine), __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-  }
-  // 2. this workgroup's share of the int8 token quantization (read by the next launches)
+  for (int t = 1; t < Q; ++t)
+    if (lane == t) mine = lg[t];
+  if (lane < a.q) a.logits[(size_t)lane * a.E + e] = mine;
+  // this workgroup's share of the int8 token quantization
   const int nblk = a.q * a.nb_h;
   const int b_end = min((int)(blockIdx.x + 1) * a.quant_per_wg, nblk);
-  for (int b = blockIdx.x * a.quant_per_wg + tid; b < b_end; b += blockDim.x) {
+  for (int b = blockIdx.x * a.quant_per_wg + lane; b < b_end; b += blockDim.x) {
     float v[32];
     const float4* src = reinterpret_cast<const float4*>(a.x + (size_t)b * 32);
 #pragma unroll
@@ -116,83 +105,95 @@ __global__ __launch_bounds__(256) void k_route(DecodeArgs a) {
     dst[1] = make_uint4(qv[4], qv[5], qv[6], qv[7]);
     a.dx[b] = d;
   }
-  // 3. the last workgroup to get here does the top-k and the plan
-  wait_vmem();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kCtrlRouterDone], 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (done == (uint32_t)a.n_router - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
+}
+
+// ------------------------------------------------------------ top-k and plan (per workgroup)
+struct PlanLds {
+  int ids[4][8];        // selected experts per token, ascending
+  float w[4][8];        // their routing weights
+  int U;
+  int pid[kPlanMax];    // plan: expert ids ascending
+  uint32_t pmask[kPlanMax];
+  float pw[kPlanMax][4];
+};
+
+// Waves t < q select the top-k of token t; then wave 0 builds the plan from the
+// q*k (token, expert) candidates held one per lane: a candidate is the first of
+// its expert id if no lower lane holds the same id, and its plan slot is the
+// number of distinct ids smaller than its own. Every thread returns after the
+// plan is complete in LDS. `write` also stores the routing and the plan.
+__device__ void topk_and_plan(const DecodeArgs& a, PlanLds& P, bool write) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (wave < a.q) {
     int sel[8];
-    float g[8];
-    topk_wave<true>(a.logits + (size_t)wave * a.E, a.E, a.K, lane, sel, g);
+    float gv;
+    topk_wave<false>(a.logits + (size_t)wave * a.E, a.E, a.K, lane, sel, gv);
     if (lane < a.K) {
       int sv = sel[0];
-      float gv = g[0];
 #pragma unroll
       for (int k = 1; k < 8; ++k)
-        if (lane == k) {
-          sv = sel[k];
-          gv = g[k];
-        }
-      a.idx[wave * a.K + lane] = sv;
-      a.gw[wave * a.K + lane] = gv;
-      s_ids[wave][lane] = sv;
-      s_w[wave][lane] = gv;
+        if (lane == k) sv = sel[k];
+      P.ids[wave][lane] = sv;
+      P.w[wave][lane] = gv;
+      if (write) {
+        a.idx[wave * a.K + lane] = sv;
+        a.gw[wave * a.K + lane] = gv;
+      }
     }
   }
   __syncthreads();
-  // Plan, in wave 0: one (token, expert) candidate per lane. A candidate is the
-  // first of its expert id if no lower lane holds the same id; its plan slot is
-  // the number of distinct ids smaller than its own.
   if (wave == 0) {
     const int n = a.q * a.K;
     const bool have = lane < n;
-    const int t = have ? lane / a.K : 0;
-    const int k = have ? lane - t * a.K : 0;
-    const int ex = have ? s_ids[t][k] : 0x7FFFFFFF;
+    int t = 0, k = lane;
+    while (t < 3 && k >= a.K) {   // lane = t * K + k
+      k -= a.K;
+      ++t;
+    }
+    const int ex = have ? P.ids[t][k] : 0x7FFFFFFF;
     bool first = have;
     uint32_t mask = 0;
     float w4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int j = 0; j < n; ++j) {
-      const int tj = j / a.K, kj = j - tj * a.K;
-      if (s_ids[tj][kj] == ex) {
-        mask |= 1u << tj;
-        const float wj = s_w[tj][kj];
-        if (tj == 0) w4[0] = wj;
-        if (tj == 1) w4[1] = wj;
-        if (tj == 2) w4[2] = wj;
-        if (tj == 3) w4[3] = wj;
-        if (j < lane) first = false;
-      }
-    }
+    for (int tj = 0, j = 0; tj < a.q; ++tj)
+      for (int kj = 0; kj < a.K; ++kj, ++j)
+        if (P.ids[tj][kj] == ex) {
+          mask |= 1u << tj;
+          const float wj = P.w[tj][kj];
+          if (tj == 0) w4[0] = wj;
+          if (tj == 1) w4[1] = wj;
+          if (tj == 2) w4[2] = wj;
+          if (tj == 3) w4[3] = wj;
+          if (j < lane) first = false;
+        }
     const uint64_t firsts = __ballot(first);
     int slot = 0;
-    for (int j = 0; j < n; ++j) {
-      const int tj = j / a.K;
-      if (((firsts >> j) & 1ull) && s_ids[tj][j - tj * a.K] < ex) ++slot;
-    }
+    for (int tj = 0, j = 0; tj < a.q; ++tj)
+      for (int kj = 0; kj < a.K; ++kj, ++j)
+        if (((firsts >> j) & 1ull) && P.ids[tj][kj] < ex) ++slot;
     const int U = __popcll(firsts);
-    if (lane < kPlanMax && lane >= U) {        // unused slots
-      a.plan[kPlanIdOff + lane] = -1;
-      a.plan[kPlanMaskOff + lane] = 0;
-    }
     if (first) {
-      a.plan[kPlanIdOff + slot] = ex;
-      a.plan[kPlanMaskOff + slot] = (int)mask;
-      float* pw = reinterpret_cast<float*>(a.plan + kPlanWOff) + 4 * slot;
+      P.pid[slot] = ex;
+      P.pmask[slot] = mask;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) pw[c] = w4[c];
+      for (int c = 0; c < 4; ++c) P.pw[slot][c] = w4[c];
     }
-    if (lane == 0) {
-      a.plan[0] = U;
-      a.ctrl[kCtrlRouterDone] = 0;             // ready for the next call
+    if (lane == 0) P.U = U;
+    if (write) {
+      if (lane < kPlanMax && lane >= U) {
+        a.plan[kPlanIdOff + lane] = -1;
+        a.plan[kPlanMaskOff + lane] = 0;
+      }
+      if (first) {
+        a.plan[kPlanIdOff + slot] = ex;
+        a.plan[kPlanMaskOff + slot] = (int)mask;
+        float* pw = reinterpret_cast<float*>(a.plan + kPlanWOff) + 4 * slot;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) pw[c] = w4[c];
+      }
+      if (lane == 0) a.plan[0] = U;
     }
   }
+  __syncthreads();
 }
 
 // ------------------------------------------------------------ k_gateup
@@ -203,11 +204,12 @@ __global__ __launch_bounds__(512) void k_gateup(DecodeArgs a) {
   constexpr int NBL = (FMT == 4) ? 1 : 2;
   constexpr int RPW = 4;
   __shared__ float s_a[4][32];
+  __shared__ PlanLds P;
   const int u = blockIdx.y, rb = blockIdx.x;
-  const int U = a.plan[0];
-  if (u >= U) return;
-  const int e = a.plan[kPlanIdOff + u];
-  const uint32_t mask = (uint32_t)a.plan[kPlanMaskOff + u];
+  topk_and_plan(a, P, blockIdx.x == 0 && blockIdx.y == 0);
+  if (u >= P.U) return;
+  const int e = P.pid[u];
+  const uint32_t mask = P.pmask[u];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row0 = rb * 32 + wave * RPW;
   const uint8_t* gbase = a.gate + (size_t)e * a.gu_stride;
@@ -292,8 +294,13 @@ __global__ __launch_bounds__(256) void k_down(DecodeArgs a) {
   const int sub = lane >> lpr_log2, sl = lane & (lpr - 1);
   const int row = (blockIdx.x * 4 + wave) * (64 >> lpr_log2) + sub;
   const bool row_ok = row < a.hidden;
-  const int U = a.plan[0];
-  const float* pw = reinterpret_cast<const float*>(a.plan + kPlanWOff);
+  // the plan (256 words: size, ids, masks, weights), read in one round trip
+  static_assert(kPlanWOff + 4 * kPlanMax == 256, "plan fits one load per thread");
+  __shared__ int s_plan[kPlanWOff + 4 * kPlanMax];
+  s_plan[threadIdx.x] = a.plan[threadIdx.x];
+  __syncthreads();
+  const int U = s_plan[0];
+  const float* pw = reinterpret_cast<const float*>(s_plan + kPlanWOff);
   const int nb = a.nb_i;
   float acc[Q];
 #pragma unroll
@@ -306,14 +313,14 @@ __global__ __launch_bounds__(256) void k_down(DecodeArgs a) {
       int ej[UB];
 #pragma unroll
       for (int j = 0; j < UB; ++j) {
-        ej[j] = (u0 + j < U) ? a.plan[kPlanIdOff + u0 + j] : 0;
+        ej[j] = (u0 + j < U) ? s_plan[kPlanIdOff + u0 + j] : 0;
         if (ok && u0 + j < U) bl[j].load(a.down + (size_t)ej[j] * a.dn_stride + (size_t)row * a.dn_row_bytes, nb, b);
       }
 #pragma unroll
       for (int j = 0; j < UB; ++j) {
         const int u = u0 + j;
         if (u < U) {
-          const uint32_t mask = (uint32_t)a.plan[kPlanMaskOff + u];
+          const uint32_t mask = (uint32_t)s_plan[kPlanMaskOff + u];
           uint32_t cb[4];
           load_codebook<FMT>(a.cb_down + ((size_t)ej[j] << FMT), cb);
           if (ok) {
@@ -348,7 +355,7 @@ template <int FG, int FD, int Q>
 int launch_decode_t(const DecodeArgs& a, int U_max, hipStream_t s) {
   {
     KernelTimer kt("route", s);
-    hipLaunchKernelGGL(k_route<Q>, dim3(a.n_router), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_route<Q>, dim3(a.E), dim3(64), 0, s, a);
   }
   int st = launch_check("route");
   if (st) return st;
@@ -426,8 +433,7 @@ extern "C" int qmoe_decode_layer(const qmoe_layer* L, const float* x, int32_t q,
   a.dn_row_bytes = (size_t)a.nb_i * fd.block_bytes;
   a.dn_stride = a.dn_row_bytes * L->hidden;
   a.dn_lpr_log2 = ilog2(lanes_per_row(a.nb_i, L->fmt_down == QMOE_FP4 ? 1 : 2));
-  a.n_router = (L->n_experts + 3) / 4;
-  a.quant_per_wg = (q * a.nb_h + a.n_router - 1) / a.n_router;
+  a.quant_per_wg = (q * a.nb_h + L->n_experts - 1) / L->n_experts;
   const int U_max = std::min(q * L->topk, L->n_experts);
   hipStream_t s = as_stream(stream);
   switch (q) {

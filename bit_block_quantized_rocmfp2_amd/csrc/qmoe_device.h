@@ -172,9 +172,23 @@ __device__ __forceinline__ int block_dot(const uint32_t w[8], const uint32_t x[8
   return acc;
 }
 
-// Sum over groups of `lpr` adjacent lanes (lpr a power of two <= 64).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over groups of `lpr` adjacent lanes (lpr a power of two <= 64); every lane
+// of a group gets the group's sum. Exchanges inside 16-lane rows use DPP (lane
+// ^ 1, lane ^ 2, then the half-row and row mirrors, which pair lanes whose
+// partial sums are already uniform over the smaller group), the rest use
+// ds_bpermute. The addition order is fixed, so results are deterministic.
 __device__ __forceinline__ float group_sum(float v, int lpr) {
-  for (int m = lpr >> 1; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  if (lpr >= 2) v += dpp_f32<0xB1>(v);     // quad_perm [1,0,3,2]
+  if (lpr >= 4) v += dpp_f32<0x4E>(v);     // quad_perm [2,3,0,1]
+  if (lpr >= 8) v += dpp_f32<0x141>(v);    // row_half_mirror
+  if (lpr >= 16) v += dpp_f32<0x140>(v);   // row_mirror
+  if (lpr >= 32) v += __shfl_xor(v, 16);
+  if (lpr >= 64) v += __shfl_xor(v, 32);
   return v;
 }
 
@@ -298,66 +312,95 @@ __device__ __forceinline__ void router_wave(const uint16_t* __restrict__ W, cons
 // ---------------------------------------------------------------------------
 // Top-k of one token's E logits (one wave, K <= 8, E <= 512). Equal logits go
 // to the lower id. Every lane ends with the selected ids in ascending order in
-// sel[0..K) (unused entries 0x7FFFFFFF) and the softmax over the selected
-// logits (fp64, max subtracted, summed in ascending id order) in g[0..K).
+// sel[0..K) (unused entries 0x7FFFFFFF); lane k < K also gets g_mine, the
+// softmax weight of sel[k] (fp64, max subtracted, sum in ascending id order).
+//
+// Logits are compared as order-preserving 64-bit keys (-0.0 folded into +0.0 so
+// that equal values tie); a round takes the wave maximum of the keys (DPP lane
+// exchanges inside 16-lane rows, then two cross-row exchanges) and resolves the
+// lowest id holding it with one ballot per candidate slot.
 constexpr int kTopkMaxPerLane = 8;   // E <= 512
 
-__device__ __forceinline__ bool topk_better(double av, int ai, double bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
+__device__ __forceinline__ uint64_t f64_order_key(double v) {
+  if (v == 0.0) v = 0.0;   // -0.0 -> +0.0
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ double f64_from_order_key(uint64_t k) {
+  const uint64_t b = (k >> 63) ? (k ^ 0x8000000000000000ull) : ~k;
+  return __longlong_as_double((long long)b);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, 0xF, 0xF, true);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp_u64<0xB1>(v);  v = o > v ? o : v;    // quad_perm [1,0,3,2]: lane ^ 1
+  o = dpp_u64<0x4E>(v);  v = o > v ? o : v;    // quad_perm [2,3,0,1]: lane ^ 2
+  o = dpp_u64<0x141>(v); v = o > v ? o : v;    // row_half_mirror: quads 0 <-> 1 of each 8
+  o = dpp_u64<0x140>(v); v = o > v ? o : v;    // row_mirror: halves of each 16-lane row
+  o = ((uint64_t)(uint32_t)__shfl_xor((int)(v >> 32), 16) << 32) | (uint32_t)__shfl_xor((int)(uint32_t)v, 16);
+  v = o > v ? o : v;
+  o = ((uint64_t)(uint32_t)__shfl_xor((int)(v >> 32), 32) << 32) | (uint32_t)__shfl_xor((int)(uint32_t)v, 32);
+  v = o > v ? o : v;
+  return v;
 }
 
 // COHERENT = true reads the logits with agent-scope atomic loads (they were
 // written by other workgroups of the same launch).
 template <bool COHERENT = false>
 __device__ __forceinline__ void topk_wave(const double* __restrict__ row, int E, int K, int lane, int sel[8],
-                                          float g[8]) {
-  double v[kTopkMaxPerLane];
+                                          float& g_mine) {
+  uint64_t key[kTopkMaxPerLane];
 #pragma unroll
   for (int j = 0; j < kTopkMaxPerLane; ++j) {
     const int e = lane + 64 * j;
+    key[j] = 0;   // no candidate (no real logit maps to key 0)
     if (e < E) {
+      double v;
       if constexpr (COHERENT)
-        v[j] = __longlong_as_double((long long)__hip_atomic_load(reinterpret_cast<const uint64_t*>(row) + e,
-                                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        v = __longlong_as_double((long long)__hip_atomic_load(reinterpret_cast<const uint64_t*>(row) + e,
+                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       else
-        v[j] = row[e];
-    } else {
-      v[j] = -INFINITY;
+        v = row[e];
+      key[j] = f64_order_key(v);
     }
   }
-  uint32_t taken = 0;
-  double sv[8];
+  uint64_t sk[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     sel[k] = 0x7FFFFFFF;
-    sv[k] = -INFINITY;
+    sk[k] = 0;
     if (k < K) {
-      double bv = -INFINITY;
-      int bi = 0x7FFFFFFF;
+      uint64_t lk = 0;
 #pragma unroll
-      for (int j = 0; j < kTopkMaxPerLane; ++j) {
-        const int e = lane + 64 * j;
-        if (e < E && !((taken >> j) & 1u) && topk_better(v[j], e, bv, bi)) {
-          bv = v[j];
-          bi = e;
-        }
-      }
+      for (int j = 0; j < kTopkMaxPerLane; ++j)
+        if (64 * j < E) lk = key[j] > lk ? key[j] : lk;
+      const uint64_t gk = wave_max_u64(lk);
+      int pick = 0x7FFFFFFF;
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const double ov = __shfl_xor(bv, m);
-        const int oi = __shfl_xor(bi, m);
-        if (topk_better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
+      for (int j = kTopkMaxPerLane - 1; j >= 0; --j)
+        if (64 * j < E) {
+          const uint64_t m = __ballot(key[j] == gk);
+          if (m) pick = 64 * j + (int)__builtin_ctzll(m);
         }
+      sel[k] = pick;
+      sk[k] = gk;
+      if ((pick & 63) == lane) {
+#pragma unroll
+        for (int j = 0; j < kTopkMaxPerLane; ++j)
+          if (j == (pick >> 6)) key[j] = 0;
       }
-      sel[k] = bi;
-      sv[k] = bv;
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     }
   }
-  const double m = sv[0];                      // the first pick is the largest logit
-  // ascending ids: odd-even transposition sort of the 8 (id, logit) pairs
+  const double m = f64_from_order_key(sk[0]);   // the first pick is the largest logit
+  // ascending ids: odd-even transposition sort of the 8 (id, key) pairs
 #pragma unroll
   for (int r = 0; r < 8; ++r)
 #pragma unroll
@@ -366,18 +409,26 @@ __device__ __forceinline__ void topk_wave(const double* __restrict__ row, int E,
         const int ti = sel[i];
         sel[i] = sel[i + 1];
         sel[i + 1] = ti;
-        const double tv = sv[i];
-        sv[i] = sv[i + 1];
-        sv[i + 1] = tv;
+        const uint64_t tk = sk[i];
+        sk[i] = sk[i + 1];
+        sk[i + 1] = tk;
       }
-  double ex[8], S = 0.0;
+  // lane k < K: exp of its own selected logit; the sum in ascending id order
+  uint64_t my = sk[0];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    ex[k] = (k < K) ? exp(sv[k] - m) : 0.0;
-    if (k < K) S = S + ex[k];
-  }
+  for (int k = 1; k < 8; ++k)
+    if (lane == k) my = sk[k];
+  const double ex = (lane < K) ? exp(f64_from_order_key(my) - m) : 0.0;
+  const uint64_t exb = (uint64_t)__double_as_longlong(ex);
+  double S = 0.0;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) g[k] = (k < K) ? (float)(ex[k] / S) : 0.0f;
+  for (int k = 0; k < 8; ++k)
+    if (k < K) {
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)exb, k);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(exb >> 32), k);
+      S = S + __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+    }
+  g_mine = (lane < K) ? (float)(ex / S) : 0.0f;
 }
 
 }  // namespace qk

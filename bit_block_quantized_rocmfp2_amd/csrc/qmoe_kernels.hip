@@ -73,19 +73,15 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits,
   const int t = blockIdx.x * 4 + wave;
   if (t >= ntok) return;
   int sel[8];
-  float g[8];
-  topk_wave(logits + (size_t)t * E, E, K, lane, sel, g);
-  if (lane < 8 && lane < K) {
+  float gm;
+  topk_wave(logits + (size_t)t * E, E, K, lane, sel, gm);
+  if (lane < K) {
     int sv = sel[0];
-    float gv = g[0];
 #pragma unroll
     for (int k = 1; k < 8; ++k)
-      if (lane == k) {
-        sv = sel[k];
-        gv = g[k];
-      }
+      if (lane == k) sv = sel[k];
     idx[(size_t)t * K + lane] = sv;
-    gw[(size_t)t * K + lane] = gv;
+    gw[(size_t)t * K + lane] = gm;
   }
 }
 
