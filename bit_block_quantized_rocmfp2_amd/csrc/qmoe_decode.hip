@@ -109,107 +109,140 @@ __global__ __launch_bounds__(64) void k_route(DecodeArgs a) {
 
 // ------------------------------------------------------------ top-k and plan (per workgroup)
 struct PlanLds {
-  int ids[4][8];        // selected experts per token, ascending
-  float w[4][8];        // their routing weights
-  int U;
-  int pid[kPlanMax];    // plan: expert ids ascending
-  uint32_t pmask[kPlanMax];
-  float pw[kPlanMax][4];
+  uint32_t bits[4][16];   // per token: bitmap of its selected experts (E <= 512)
+  int ids[4][8];          // plan writer only: selected ids of token t, ascending
+  float w[4][8];          // plan writer only: their routing weights
+  int e;                  // one token: the expert of this workgroup's plan slot
 };
 
-// Waves t < q select the top-k of token t; then wave 0 builds the plan from the
-// q*k (token, expert) candidates held one per lane: a candidate is the first of
-// its expert id if no lower lane holds the same id, and its plan slot is the
-// number of distinct ids smaller than its own. Every thread returns after the
-// plan is complete in LDS. `write` also stores the routing and the plan.
-__device__ void topk_and_plan(const DecodeArgs& a, PlanLds& P, bool write) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (wave < a.q) {
-    int sel[8];
-    float gv;
-    topk_wave<false>(a.logits + (size_t)wave * a.E, a.E, a.K, lane, sel, gv);
-    if (lane < a.K) {
-      int sv = sel[0];
-#pragma unroll
-      for (int k = 1; k < 8; ++k)
-        if (lane == k) sv = sel[k];
-      P.ids[wave][lane] = sv;
-      P.w[wave][lane] = gv;
+// Every workgroup selects the experts itself. With one token wave 0 runs the
+// top-k and passes the expert of slot u (the plan is the K ids ascending with
+// column mask 1) to the other waves through LDS. With q > 1 tokens, waves t < q select token t and set its
+// experts in an LDS bitmap; after one barrier every wave reads the union of the
+// bitmaps: plan slot s holds the s-th set bit, i.e. the distinct ids in
+// ascending order, and its column mask is that bit across the tokens. Returns
+// the expert of plan slot u (-1 if u is beyond the plan) and its column mask.
+// `write` (one workgroup) also computes the routing weights and stores the
+// routing (idx, gw) and the plan (size, ids, masks, weights per column).
+template <int Q>
+__device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, int u, bool write, uint32_t& mask) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  TopkPick p;
+  if constexpr (Q == 1) {
+    if (wave == 0) {
+      const uint64_t first = topk_select(a.logits, a.E, a.K, lane, p);
+      const int eu = (u < a.K) ? __builtin_amdgcn_readlane(p.id, topk_lane_of_rank(p, u)) : -1;
+      if (lane == 0) P.e = eu;
       if (write) {
-        a.idx[wave * a.K + lane] = sv;
-        a.gw[wave * a.K + lane] = gv;
-      }
-    }
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const int n = a.q * a.K;
-    const bool have = lane < n;
-    int t = 0, k = lane;
-    while (t < 3 && k >= a.K) {   // lane = t * K + k
-      k -= a.K;
-      ++t;
-    }
-    const int ex = have ? P.ids[t][k] : 0x7FFFFFFF;
-    bool first = have;
-    uint32_t mask = 0;
-    float w4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int tj = 0, j = 0; tj < a.q; ++tj)
-      for (int kj = 0; kj < a.K; ++kj, ++j)
-        if (P.ids[tj][kj] == ex) {
-          mask |= 1u << tj;
-          const float wj = P.w[tj][kj];
-          if (tj == 0) w4[0] = wj;
-          if (tj == 1) w4[1] = wj;
-          if (tj == 2) w4[2] = wj;
-          if (tj == 3) w4[3] = wj;
-          if (j < lane) first = false;
+        const float g = topk_softmax(p, first, a.K, lane);
+        if (lane < a.K) {
+          a.idx[p.rank] = p.id;
+          a.gw[p.rank] = g;
+          a.plan[kPlanIdOff + p.rank] = p.id;
+          a.plan[kPlanMaskOff + p.rank] = 1;
+          reinterpret_cast<float4*>(a.plan + kPlanWOff)[p.rank] = make_float4(g, 0.0f, 0.0f, 0.0f);
         }
-    const uint64_t firsts = __ballot(first);
-    int slot = 0;
-    for (int tj = 0, j = 0; tj < a.q; ++tj)
-      for (int kj = 0; kj < a.K; ++kj, ++j)
-        if (((firsts >> j) & 1ull) && P.ids[tj][kj] < ex) ++slot;
-    const int U = __popcll(firsts);
-    if (first) {
-      P.pid[slot] = ex;
-      P.pmask[slot] = mask;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) P.pw[slot][c] = w4[c];
-    }
-    if (lane == 0) P.U = U;
-    if (write) {
-      if (lane < kPlanMax && lane >= U) {
-        a.plan[kPlanIdOff + lane] = -1;
-        a.plan[kPlanMaskOff + lane] = 0;
+        if (lane == 0) a.plan[0] = a.K;
       }
-      if (first) {
-        a.plan[kPlanIdOff + slot] = ex;
-        a.plan[kPlanMaskOff + slot] = (int)mask;
-        float* pw = reinterpret_cast<float*>(a.plan + kPlanWOff) + 4 * slot;
+    }
+    __syncthreads();
+    mask = 1u;
+    return P.e;
+  } else {
+    if (tid < 64) (&P.bits[0][0])[tid] = 0u;
+    __syncthreads();
+    if (wave < a.q) {
+      const uint64_t first = topk_select(a.logits + (size_t)wave * a.E, a.E, a.K, lane, p);
+      if (lane < a.K) atomicOr(&P.bits[wave][p.id >> 5], 1u << (p.id & 31));
+      if (write) {
+        const float g = topk_softmax(p, first, a.K, lane);
+        if (lane < a.K) {
+          P.ids[wave][p.rank] = p.id;
+          P.w[wave][p.rank] = g;
+          a.idx[wave * a.K + p.rank] = p.id;
+          a.gw[wave * a.K + p.rank] = g;
+        }
+      }
+    }
+    __syncthreads();
+    const int nw = (a.E + 31) >> 5;
+    uint32_t uw = 0;   // lane l < nw: word l of the union bitmap
+    if (lane < nw)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) pw[c] = w4[c];
+      for (int t = 0; t < Q; ++t)
+        if (t < a.q) uw |= P.bits[t][lane];
+    // slot u: uniform walk over the words
+    int e = -1, rem = u, U = 0;
+    for (int w = 0; w < nw; ++w) {
+      const uint32_t word = (uint32_t)__builtin_amdgcn_readlane(uw, w);
+      const int c = __popc(word);
+      if (e < 0 && rem < c) {
+        uint32_t x = word;
+        for (int i = 0; i < rem; ++i) x &= x - 1;
+        e = 32 * w + (int)__builtin_ctz(x);
+      }
+      if (e < 0) rem -= c;
+      U += c;
+    }
+    mask = 0;
+    if (e >= 0)
+#pragma unroll
+      for (int t = 0; t < Q; ++t)
+        if (t < a.q && (P.bits[t][e >> 5] >> (e & 31) & 1u)) mask |= 1u << t;
+    if (write && wave == 0) {
+      // lane s < U: the s-th distinct expert, its mask and weights
+      int es = -1, rs = lane;
+      for (int w = 0; w < nw; ++w) {
+        const uint32_t word = (uint32_t)__builtin_amdgcn_readlane(uw, w);
+        const int c = __popc(word);
+        if (es < 0 && rs < c) {
+          uint32_t x = word;
+          for (int i = 0; i < rs; ++i) x &= x - 1;
+          es = 32 * w + (int)__builtin_ctz(x);
+        }
+        if (es < 0) rs -= c;
+      }
+      if (lane < kPlanMax) {
+        uint32_t ms = 0;
+        float4 ws = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (es >= 0)
+#pragma unroll
+          for (int t = 0; t < Q; ++t)
+            if (t < a.q && (P.bits[t][es >> 5] >> (es & 31) & 1u)) {
+              ms |= 1u << t;
+              float wt = 0.0f;
+#pragma unroll
+              for (int k = 0; k < 8; ++k)
+                if (k < a.K && P.ids[t][k] == es) wt = P.w[t][k];
+              if (t == 0) ws.x = wt;
+              if (t == 1) ws.y = wt;
+              if (t == 2) ws.z = wt;
+              if (t == 3) ws.w = wt;
+            }
+        a.plan[kPlanIdOff + lane] = es;
+        a.plan[kPlanMaskOff + lane] = (int)ms;
+        reinterpret_cast<float4*>(a.plan + kPlanWOff)[lane] = ws;
       }
       if (lane == 0) a.plan[0] = U;
     }
+    return e;
   }
-  __syncthreads();
 }
 
 // ------------------------------------------------------------ k_gateup
 // 8 waves; wave w owns rows 4w..4w+3 of both gate and up of the workgroup's 32
 // rows. Lanes cover NBL consecutive blocks each.
 template <int FMT, int Q>
-__global__ __launch_bounds__(512) void k_gateup(DecodeArgs a) {
+__global__ __launch_bounds__(512, (Q == 1) ? 2 : 1) void k_gateup(DecodeArgs a) {
   constexpr int NBL = (FMT == 4) ? 1 : 2;
   constexpr int RPW = 4;
   __shared__ float s_a[4][32];
   __shared__ PlanLds P;
   const int u = blockIdx.y, rb = blockIdx.x;
-  topk_and_plan(a, P, blockIdx.x == 0 && blockIdx.y == 0);
-  if (u >= P.U) return;
-  const int e = P.pid[u];
-  const uint32_t mask = P.pmask[u];
+  uint32_t mask;
+  const int e = topk_and_plan<Q>(a, P, u, blockIdx.x == 0 && blockIdx.y == 0, mask);
+  if (e < 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row0 = rb * 32 + wave * RPW;
   const uint8_t* gbase = a.gate + (size_t)e * a.gu_stride;

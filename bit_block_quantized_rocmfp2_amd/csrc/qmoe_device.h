@@ -311,14 +311,11 @@ __device__ __forceinline__ void router_wave(const uint16_t* __restrict__ W, cons
 
 // ---------------------------------------------------------------------------
 // Top-k of one token's E logits (one wave, K <= 8, E <= 512). Equal logits go
-// to the lower id. Every lane ends with the selected ids in ascending order in
-// sel[0..K) (unused entries 0x7FFFFFFF); lane k < K also gets g_mine, the
-// softmax weight of sel[k] (fp64, max subtracted, sum in ascending id order).
-//
-// Logits are compared as order-preserving 64-bit keys (-0.0 folded into +0.0 so
-// that equal values tie); a round takes the wave maximum of the keys (DPP lane
-// exchanges inside 16-lane rows, then two cross-row exchanges) and resolves the
-// lowest id holding it with one ballot per candidate slot.
+// to the lower id. Logits are compared as order-preserving 64-bit keys (-0.0
+// folded into +0.0 so that equal values tie). A selection round reduces only the
+// 32-bit high words across the wave (DPP exchanges inside 16-lane rows, then the
+// four row maxima); the full keys are compared only when several candidates
+// share the largest high word.
 constexpr int kTopkMaxPerLane = 8;   // E <= 512
 
 __device__ __forceinline__ uint64_t f64_order_key(double v) {
@@ -352,83 +349,132 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-// COHERENT = true reads the logits with agent-scope atomic loads (they were
-// written by other workgroups of the same launch).
-template <bool COHERENT = false>
-__device__ __forceinline__ void topk_wave(const double* __restrict__ row, int E, int K, int lane, int sel[8],
-                                          float& g_mine) {
-  uint64_t key[kTopkMaxPerLane];
+// Wave-wide maximum of a uint32 (uniform result): four DPP exchanges give every
+// lane its 16-lane row's maximum, then the four row maxima are combined.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x140, 0xF, 0xF, true));
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane(v, 0), (uint32_t)__builtin_amdgcn_readlane(v, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane(v, 32), (uint32_t)__builtin_amdgcn_readlane(v, 48));
+  return max(a, b);
+}
+
+// Top-k of one row of E fp64 logits (E <= 512, K <= 8) by one wave; lane l holds
+// logits l, l+64, ... as order keys. Each of the K rounds first finds the largest
+// high word of the remaining keys; when exactly one key carries it, that key is
+// the maximum. Otherwise the candidates sharing the high word are compared on the
+// full 64-bit key and the lowest id among equal keys wins (the oracle's tie
+// rule). Lane k < K ends with the k-th pick: its id, its key and its rank among
+// the picks in ascending id order (lanes >= K: id 0x7FFFFFFF, key 0, rank 8).
+// Returns the key of the first pick, the largest logit. The row is read with
+// plain loads: it must have been written by an earlier launch.
+struct TopkPick {
+  int id;
+  uint64_t key;
+  int rank;
+};
+
+// NS = slots per lane (E <= 64 * NS); keys of ids >= E are 0 and never win.
+template <int NS>
+__device__ __forceinline__ uint64_t topk_select_ns(const double* __restrict__ row, int E, int K, int lane,
+                                                   TopkPick& p) {
+  uint64_t key[NS];
 #pragma unroll
-  for (int j = 0; j < kTopkMaxPerLane; ++j) {
+  for (int j = 0; j < NS; ++j) {
     const int e = lane + 64 * j;
-    key[j] = 0;   // no candidate (no real logit maps to key 0)
-    if (e < E) {
-      double v;
-      if constexpr (COHERENT)
-        v = __longlong_as_double((long long)__hip_atomic_load(reinterpret_cast<const uint64_t*>(row) + e,
-                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      else
-        v = row[e];
-      key[j] = f64_order_key(v);
-    }
+    key[j] = (e < E) ? f64_order_key(row[e]) : 0;   // key 0: no candidate (no real logit maps to 0)
   }
-  uint64_t sk[8];
+  p.id = 0x7FFFFFFF;
+  p.key = 0;
+  uint64_t first = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    sel[k] = 0x7FFFFFFF;
-    sk[k] = 0;
-    if (k < K) {
+    if (k >= K) break;
+    uint32_t lh = 0;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) lh = max(lh, (uint32_t)(key[j] >> 32));
+    const uint32_t gh = wave_max_u32(lh);
+    // this lane's candidates: keys whose high word is the maximum
+    int cs = -1, cnt = 0;
+    uint32_t clo = 0;
+#pragma unroll
+    for (int j = NS - 1; j >= 0; --j)
+      if ((uint32_t)(key[j] >> 32) == gh) {
+        cs = j;
+        clo = (uint32_t)key[j];
+        ++cnt;
+      }
+    const uint64_t b = __ballot(cs >= 0);
+    const uint64_t multi = __ballot(cnt > 1);
+    int pick;
+    uint64_t gk;
+    if (multi == 0 && __popcll(b) == 1) {   // one candidate: it is the maximum
+      const int L = (int)__builtin_ctzll(b);
+      pick = 64 * __builtin_amdgcn_readlane(cs, L) + L;
+      gk = ((uint64_t)gh << 32) | (uint32_t)__builtin_amdgcn_readlane(clo, L);
+    } else {   // equal high words: compare full keys, lowest id among equal keys
       uint64_t lk = 0;
 #pragma unroll
-      for (int j = 0; j < kTopkMaxPerLane; ++j)
-        if (64 * j < E) lk = key[j] > lk ? key[j] : lk;
-      const uint64_t gk = wave_max_u64(lk);
-      int pick = 0x7FFFFFFF;
+      for (int j = 0; j < NS; ++j)
+        if ((uint32_t)(key[j] >> 32) == gh) lk = key[j] > lk ? key[j] : lk;
+      gk = wave_max_u64(lk);
+      pick = 0x7FFFFFFF;
 #pragma unroll
-      for (int j = kTopkMaxPerLane - 1; j >= 0; --j)
-        if (64 * j < E) {
-          const uint64_t m = __ballot(key[j] == gk);
-          if (m) pick = 64 * j + (int)__builtin_ctzll(m);
-        }
-      sel[k] = pick;
-      sk[k] = gk;
-      if ((pick & 63) == lane) {
-#pragma unroll
-        for (int j = 0; j < kTopkMaxPerLane; ++j)
-          if (j == (pick >> 6)) key[j] = 0;
+      for (int j = NS - 1; j >= 0; --j) {
+        const uint64_t m = __ballot(key[j] == gk);
+        if (m) pick = 64 * j + (int)__builtin_ctzll(m);
       }
     }
+    if (k == 0) first = gk;
+    if (lane == k) {
+      p.id = pick;
+      p.key = gk;
+    }
+    if ((pick & 63) == lane) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+        if (j == (pick >> 6)) key[j] = 0;
+    }
   }
-  const double m = f64_from_order_key(sk[0]);   // the first pick is the largest logit
-  // ascending ids: odd-even transposition sort of the 8 (id, key) pairs
+  // rank in ascending id order: the number of picks with a smaller id
+  int r = 0;
 #pragma unroll
-  for (int r = 0; r < 8; ++r)
-#pragma unroll
-    for (int i = r & 1; i < 7; i += 2)
-      if (sel[i] > sel[i + 1]) {
-        const int ti = sel[i];
-        sel[i] = sel[i + 1];
-        sel[i + 1] = ti;
-        const uint64_t tk = sk[i];
-        sk[i] = sk[i + 1];
-        sk[i + 1] = tk;
-      }
-  // lane k < K: exp of its own selected logit; the sum in ascending id order
-  uint64_t my = sk[0];
-#pragma unroll
-  for (int k = 1; k < 8; ++k)
-    if (lane == k) my = sk[k];
-  const double ex = (lane < K) ? exp(f64_from_order_key(my) - m) : 0.0;
+  for (int j = 0; j < 8; ++j)
+    if (j < K) r += (__builtin_amdgcn_readlane(p.id, j) < p.id) ? 1 : 0;
+  p.rank = (lane < K) ? r : 8;
+  return first;
+}
+
+__device__ __forceinline__ uint64_t topk_select(const double* __restrict__ row, int E, int K, int lane, TopkPick& p) {
+  if (E <= 64) return topk_select_ns<1>(row, E, K, lane, p);
+  if (E <= 256) return topk_select_ns<4>(row, E, K, lane, p);
+  return topk_select_ns<8>(row, E, K, lane, p);
+}
+
+// Lane holding the pick of ascending-id rank r (wave-uniform r < K).
+__device__ __forceinline__ int topk_lane_of_rank(const TopkPick& p, int r) {
+  return (int)__builtin_ctzll(__ballot(p.rank == r));
+}
+
+// Routing weight of the pick held by lane k < K: softmax over the selected
+// logits, shifted by their maximum (key `first`), summed in ascending id order,
+// all in fp64 and rounded to fp32 once. Lanes >= K return 0.
+__device__ __forceinline__ float topk_softmax(const TopkPick& p, uint64_t first, int K, int lane) {
+  const double m = f64_from_order_key(first);
+  const double ex = (lane < K) ? exp(f64_from_order_key(p.key) - m) : 0.0;
   const uint64_t exb = (uint64_t)__double_as_longlong(ex);
   double S = 0.0;
 #pragma unroll
-  for (int k = 0; k < 8; ++k)
-    if (k < K) {
-      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)exb, k);
-      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(exb >> 32), k);
+  for (int r = 0; r < 8; ++r)
+    if (r < K) {
+      const int l = topk_lane_of_rank(p, r);
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)exb, l);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(exb >> 32), l);
       S = S + __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
     }
-  g_mine = (lane < K) ? (float)(ex / S) : 0.0f;
+  return (lane < K) ? (float)(ex / S) : 0.0f;
 }
 
 }  // namespace qk

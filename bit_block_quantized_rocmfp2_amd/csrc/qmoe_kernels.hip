@@ -72,16 +72,12 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits,
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= ntok) return;
-  int sel[8];
-  float gm;
-  topk_wave(logits + (size_t)t * E, E, K, lane, sel, gm);
+  TopkPick p;
+  const uint64_t first = topk_select(logits + (size_t)t * E, E, K, lane, p);
+  const float g = topk_softmax(p, first, K, lane);
   if (lane < K) {
-    int sv = sel[0];
-#pragma unroll
-    for (int k = 1; k < 8; ++k)
-      if (lane == k) sv = sel[k];
-    idx[(size_t)t * K + lane] = sv;
-    gw[(size_t)t * K + lane] = gm;
+    idx[(size_t)t * K + p.rank] = p.id;
+    gw[(size_t)t * K + p.rank] = g;
   }
 }
 

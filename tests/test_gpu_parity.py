@@ -140,6 +140,67 @@ def test_route_logits_bit_exact():
     assert np.array_equal(lg, router.logits(dl.w_router_host, x))
 
 
+def tied_layer(E, seed, tiny_steps):
+    """Router rows repeat with period 5, so logits tie exactly in groups; with
+    `tiny_steps` a bias of (e // 5) * 2**-40 makes the tied logits differ only in
+    their low-order bits (equal high words, distinct values)."""
+    spec = gen.LayerSpec.tiny(n_experts=E, topk=6)
+    bias = (np.arange(E) // 5).astype(np.float64) * 2.0 ** -40 if tiny_steps else None
+    dl = qm.device.DeviceLayer(spec, seed=seed, bias=bias)
+    w = dl.w_router_host.copy()
+    w[5:] = w[np.arange(5, E) % 5]
+    dl.w_router_host = w
+    dl.w_router.copy_(torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).to(dl.w_router.device))
+    return spec, dl, bias
+
+
+@pytest.mark.parametrize("tiny_steps", [False, True])
+def test_route_ties(tiny_steps):
+    spec, dl, bias = tied_layer(40, 11, tiny_steps)
+    x = gen.tokens(9, spec.hidden, seed=11)
+    idx_ref, g_ref, lg = router.route(dl.w_router_host, x, bias, spec.topk)
+    # the fixture really ties: equal logits, or (with the bias steps) equal high words of distinct logits
+    hi = lg.view(np.uint64) >> np.uint64(32)
+    assert all(len(set(hi[t].tolist())) < spec.n_experts for t in range(9))
+    assert all((len(set(lg[t].tolist())) == spec.n_experts) == tiny_steps for t in range(9))
+    idx = torch.empty((9, spec.topk), dtype=torch.int32, device="cuda")
+    gw = torch.empty((9, spec.topk), dtype=torch.float32, device="cuda")
+    qm.qmoe_route(dl.desc, dev(x), idx, gw, dl.workspace(9))
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert np.max(np.abs(gw.cpu().numpy() - g_ref)) < 1e-6
+
+
+@pytest.mark.parametrize("tiny_steps", [False, True])
+@pytest.mark.parametrize("q", [1, 3])
+def test_decode_ties(tiny_steps, q):
+    spec, dl, bias = tied_layer(40, 12, tiny_steps)
+    x = gen.tokens(q, spec.hidden, seed=12)
+    out, ws = run_decode(dl, x)
+    ref, idx_ref, g_ref = moe.moe_tokens(oracle_layer(spec, 12, dl.w_router_host, bias), x)
+    lay = qm.qmoe_workspace_layout(dl.desc, q)
+    idx = ws[lay["idx"]: lay["idx"] + 4 * q * spec.topk].cpu().numpy().view(np.int32).reshape(q, spec.topk)
+    assert np.array_equal(idx, idx_ref)
+    assert moe.rel_l2(out, ref) < TOL
+
+
+@pytest.mark.parametrize("E", [64, 65, 300, 512])
+def test_route_expert_counts(E):
+    spec = gen.LayerSpec.tiny(n_experts=E, topk=8)
+    dl = qm.device.DeviceLayer(spec, seed=13)
+    x = gen.tokens(6, spec.hidden, seed=13)
+    idx_ref, g_ref, _ = router.route(dl.w_router_host, x, None, spec.topk)
+    idx = torch.empty((6, spec.topk), dtype=torch.int32, device="cuda")
+    gw = torch.empty((6, spec.topk), dtype=torch.float32, device="cuda")
+    qm.qmoe_route(dl.desc, dev(x), idx, gw, dl.workspace(6))
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert np.max(np.abs(gw.cpu().numpy() - g_ref)) < 1e-6
+    out, _ = run_decode(dl, x[:2])
+    ref, _, _ = moe.moe_tokens(oracle_layer(spec, 13, dl.w_router_host), x[:2])
+    assert moe.rel_l2(out, ref) < TOL
+
+
 # ------------------------------------------------------------------ decode layer
 
 def run_decode(dl, x, ws=None):
