@@ -89,21 +89,17 @@ __global__ __launch_bounds__(64) void k_route(DecodeArgs a) {
   // this workgroup's share of the int8 token quantization
   const int nblk = a.q * a.nb_h;
   const int b_end = min((int)(blockIdx.x + 1) * a.quant_per_wg, nblk);
-  for (int b = blockIdx.x * a.quant_per_wg + lane; b < b_end; b += blockDim.x) {
-    float v[32];
-    const float4* src = reinterpret_cast<const float4*>(a.x + (size_t)b * 32);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float4 f = src[i];
-      v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
-    }
-    uint32_t qv[8];
+  // two blocks per pass, one per half-wave
+  for (int b0 = blockIdx.x * a.quant_per_wg; b0 < b_end; b0 += 2) {
+    const int b = b0 + (lane >> 5), j = lane & 31;
+    const bool ok = b < b_end;
+    const float v = ok ? a.x[(size_t)b * 32 + j] : 0.0f;
     float d;
-    quant_block32(v, a.rot_gateup, qv, &d);
-    uint4* dst = reinterpret_cast<uint4*>(a.xq + (size_t)b * 32);
-    dst[0] = make_uint4(qv[0], qv[1], qv[2], qv[3]);
-    dst[1] = make_uint4(qv[4], qv[5], qv[6], qv[7]);
-    a.dx[b] = d;
+    const uint32_t w = quant_block32_lanes(v, a.rot_gateup, &d);
+    if (ok) {
+      if ((j & 3) == 0) reinterpret_cast<uint32_t*>(a.xq + (size_t)b * 32)[j >> 2] = w;
+      if (j == 0) a.dx[b] = d;
+    }
   }
 }
 
@@ -298,19 +294,17 @@ __global__ __launch_bounds__(512, (Q == 1) ? 2 : 1) void k_gateup(DecodeArgs a) 
         if (lane == 0) s_a[t][wave * RPW + r] = gv / (1.0f + expf(-gv)) * uv;
       }
   __syncthreads();
-  const int t = threadIdx.x;
-  if (t < Q && (mask >> t & 1)) {
-    float v[32];
-#pragma unroll
-    for (int j = 0; j < 32; ++j) v[j] = s_a[t][j];
-    uint32_t qv[8];
+  // requantize the 32-row block: half-wave h of wave w takes column 2w + h
+  if (wave < (Q + 1) / 2) {
+    const int t = 2 * wave + (lane >> 5), j = lane & 31;
+    const bool act = t < Q && (mask >> t & 1);
     float d;
-    quant_block32(v, a.rot_down, qv, &d);
-    const size_t slot = (size_t)u * 4 + t;
-    uint4* dst = reinterpret_cast<uint4*>(a.hq + slot * a.inter + (size_t)rb * 32);
-    dst[0] = make_uint4(qv[0], qv[1], qv[2], qv[3]);
-    dst[1] = make_uint4(qv[4], qv[5], qv[6], qv[7]);
-    a.dh[slot * a.nb_i + rb] = d;
+    const uint32_t w = quant_block32_lanes(act ? s_a[t][j] : 0.0f, a.rot_down, &d);
+    if (act) {
+      const size_t slot = (size_t)u * 4 + t;
+      if ((j & 3) == 0) reinterpret_cast<uint32_t*>(a.hq + slot * a.inter + (size_t)rb * 32)[j >> 2] = w;
+      if (j == 0) a.dh[slot * a.nb_i + rb] = d;
+    }
   }
 }
 

@@ -237,6 +237,62 @@ __device__ __forceinline__ void quant_block32(float v[32], int rot, uint32_t q[8
 }
 
 
+// Exchange with lane ^ H inside each group of 32 lanes: DPP quad permutes for
+// H = 1, 2, ds_swizzle in bitmask mode (and 0x1F, xor H) for H = 4, 8, 16.
+template <int H>
+__device__ __forceinline__ float xchg32(float v) {
+  const int b = __float_as_int(v);
+  int o;
+  if constexpr (H == 1) o = __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, true);
+  else if constexpr (H == 2) o = __builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, true);
+  else o = __builtin_amdgcn_ds_swizzle(b, 0x1F | (H << 10));
+  return __int_as_float(o);
+}
+
+template <int H>
+__device__ __forceinline__ float fwht_step(float v, int j) {
+#pragma clang fp contract(off)
+  const float o = xchg32<H>(v);
+  return (j & H) ? o - v : v + o;   // (a, b) -> (a + b, a - b), a the lower index
+}
+
+// The same quantization with the 32 values of a block spread over 32 lanes:
+// lane j = lane & 31 of each half-wave holds value j (both halves may hold
+// different blocks). The butterflies, the amax and the rounding are the same
+// IEEE operations as in quant_block32, so both give identical bytes and scales.
+// All 64 lanes must be active. Returns, in lanes with j % 4 == 0, the packed
+// bytes j..j+3; *d_out is the block scale in every lane of the half.
+__device__ __forceinline__ uint32_t quant_block32_lanes(float v, int rot, float* d_out) {
+#pragma clang fp contract(off)
+  const int j = (int)(threadIdx.x & 31);
+  if (rot) {
+    v = fwht_step<1>(v, j);
+    v = fwht_step<2>(v, j);
+    v = fwht_step<4>(v, j);
+    v = fwht_step<8>(v, j);
+    v = fwht_step<16>(v, j);
+    v = v * __uint_as_float(0x3E3504F3u);
+  }
+  float m = fabsf(v);
+  m = fmaxf(m, xchg32<1>(m));
+  m = fmaxf(m, xchg32<2>(m));
+  m = fmaxf(m, xchg32<4>(m));
+  m = fmaxf(m, xchg32<8>(m));
+  m = fmaxf(m, xchg32<16>(m));
+  const float amax = fmaxf(0.0f, m);
+  const float d0 = amax / 127.0f;
+  const bool normal = d0 >= __uint_as_float(0x00800000u);   // 2^-126
+  const float id = normal ? 1.0f / d0 : 0.0f;
+  float r = rintf(v * id);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  const uint32_t b = (uint32_t)(int)r & 0xFFu;
+  // gather bytes j..j+3 into lane j (j % 4 == 0): quad_perm [1,1,3,3], then [2,2,2,2]
+  const uint32_t x1 = b | ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)b, 0xF5, 0xF, 0xF, true) << 8);
+  const uint32_t x2 = x1 | ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)x1, 0xAA, 0xF, 0xF, true) << 16);
+  *d_out = normal ? d0 : 0.0f;
+  return x2;
+}
+
 // ---------------------------------------------------------------------------
 // Router: one wave computes the fp64 logits of expert e for tokens t0..t0+TT-1.
 // Lane l holds blocks l + 64c. Per block: sequential fp64 sum of the 32 exact

@@ -238,6 +238,27 @@ def test_decode_ragged_shapes():
     assert moe.rel_l2(out, ref) < TOL
 
 
+@pytest.mark.parametrize("q,rot", [(1, 0), (3, 1), (4, 0)])
+def test_decode_token_quant_bit_exact(q, rot):
+    """The token quantization done inside the decode launch (32 lanes per block)
+    gives the oracle's bytes and scales exactly, special blocks included."""
+    spec = gen.LayerSpec.tiny(rot_gateup=rot)
+    dl = qm.device.DeviceLayer(spec, seed=9)
+    x = gen.tokens(q, spec.hidden, seed=9)
+    x[0, :32] = 0.0                                   # zero block
+    x[0, 32:64] = np.float32(1e-38)                   # subnormal scale -> zero block
+    x[-1, 64:96] = np.linspace(-3e4, 3e4, 32)         # wide range
+    x[-1, 96:128] = np.arange(32) - 15.5              # halves: ties to even
+    _, ws = run_decode(dl, x)
+    lay = qm.qmoe_workspace_layout(dl.desc, q)
+    nb = spec.hidden // 32
+    xq = ws[lay["xq"]: lay["xq"] + q * spec.hidden].cpu().numpy().view(np.int8).reshape(q, spec.hidden)
+    dx = ws[lay["dx"]: lay["dx"] + 4 * q * nb].cpu().numpy().view(np.float32).reshape(q, nb)
+    xq_ref, dx_ref = quant.quantize_act(x, rot)
+    assert np.array_equal(xq, xq_ref.reshape(q, spec.hidden))
+    assert np.array_equal(dx.view(np.uint32), dx_ref.reshape(q, nb).view(np.uint32))
+
+
 def test_decode_intermediate_activations():
     """The requantized SwiGLU output held in the workspace matches the oracle's
     int8 values except for rare one-code flips at rounding boundaries."""
