@@ -250,9 +250,25 @@ def bench_prefill(torch, qm, gen, spec, dl, dev):
     ms = t.ms / reps
     ops = 2.0 * T * spec.topk * 3 * spec.hidden * spec.inter
     tops = ops / (ms * 1e-3) / 1e12
-    log(f"prefill 8K: {ms:.3f} ms, {T / (ms * 1e-3):.0f} tok/s, {tops:.1f} TOPS")
+    qm.qmoe_timing_enable(True)
+    for _ in range(reps):
+        qm.qmoe_prefill_layer(desc, x, out, ws)
+    torch.cuda.synchronize()
+    kern = {}
+    for name in ("quant_act", "router", "topk", "group_count", "group_scan", "group_scatter", "gateup_mfma",
+                 "down_mfma", "combine"):
+        avg, _ = kernel_avg_ms(qm, name)
+        if avg:
+            kern[name] = round(avg * 1e3, 1)
+    qm.qmoe_timing_enable(False)
+    gemm_ms = (kern.get("gateup_mfma", 0) + kern.get("down_mfma", 0)) / 1e3
+    gemm_tops = ops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None
+    log(f"prefill 8K: {ms:.3f} ms, {T / (ms * 1e-3):.0f} tok/s, {tops:.1f} TOPS; kernels (us): "
+        + ", ".join(f"{k}={v}" for k, v in kern.items()))
     return {"ms_per_call": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1), "int8_TOPS": round(tops, 2),
-            "frac_int8_mfma_peak": round(tops / INT8_MFMA_PEAK_TOPS, 4)}
+            "frac_int8_mfma_peak": round(tops / INT8_MFMA_PEAK_TOPS, 4), "kernel_us": kern,
+            "gemm_int8_TOPS": round(gemm_tops, 2) if gemm_tops else None,
+            "gemm_frac_int8_mfma_peak": round(gemm_tops / INT8_MFMA_PEAK_TOPS, 4) if gemm_tops else None}
 
 
 def cpu_baseline(args, spec, dl, per_expert):

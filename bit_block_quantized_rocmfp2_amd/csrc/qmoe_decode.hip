@@ -381,20 +381,17 @@ __global__ __launch_bounds__(256) void k_down(DecodeArgs a) {
 template <int FG, int FD, int Q>
 int launch_decode_t(const DecodeArgs& a, int U_max, hipStream_t s) {
   {
-    KernelTimer kt("route", s);
-    hipLaunchKernelGGL(k_route<Q>, dim3(a.E), dim3(64), 0, s, a);
+    launch_kernel("route", k_route<Q>, dim3(a.E), dim3(64), s, a);
   }
   int st = launch_check("route");
   if (st) return st;
   {
-    KernelTimer kt("gateup", s);
-    hipLaunchKernelGGL((k_gateup<FG, Q>), dim3(a.inter / 32, U_max), dim3(512), 0, s, a);
+    launch_kernel("gateup", k_gateup<FG, Q>, dim3(a.inter / 32, U_max), dim3(512), s, a);
   }
   if ((st = launch_check("gateup"))) return st;
   const int rows_per_wg = 4 * (64 >> a.dn_lpr_log2);
   {
-    KernelTimer kt("down", s);
-    hipLaunchKernelGGL((k_down<FD, Q>), dim3((a.hidden + rows_per_wg - 1) / rows_per_wg), dim3(256), 0, s, a);
+    launch_kernel("down", k_down<FD, Q>, dim3((a.hidden + rows_per_wg - 1) / rows_per_wg), dim3(256), s, a);
   }
   return launch_check("down");
 }

@@ -302,7 +302,7 @@ __device__ __forceinline__ uint32_t quant_block32_lanes(float v, int rot, float*
 // lane j^m equals s_j + s_{j+m} for j < m). Routing: 256 experts, 6 routed
 // (lucebox.com, "Lucebox × Geometric: DeepSeek V4 Flash 0731 reaches 32.7
 // tok/s on AMD Strix Halo", section "Run with Lucebox Engine").
-constexpr int kRouterMaxC = 2;   // hidden <= 32 * 64 * 2 = 8192
+constexpr int kRouterMaxC = 4;   // blocks per lane: hidden <= 32 * 64 * 4 = 8192
 
 // On return every lane holds the logits of tokens t0..t0+TT-1 in out[] (bias
 // included; entries for tokens >= ntok are undefined).

@@ -1,5 +1,6 @@
 // Host-side helpers shared by the HIP translation units of libqmoe.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -64,17 +65,22 @@ struct WsPtrs {
 
 int ws_ptrs(const qmoe_layer* L, int32_t ntok, void* ws, size_t ws_bytes, WsPtrs* p);
 
-// Opt-in kernel timing: brackets the kernel launched in its scope with two HIP
-// events on the launch stream (see qmoe_timing_enable / qmoe_timing_read).
-class KernelTimer {
- public:
-  KernelTimer(const char* name, hipStream_t s);
-  ~KernelTimer();
+// Opt-in kernel timing (qmoe_timing_enable / qmoe_timing_read): when enabled,
+// returns a pair of events from a pool, filed under `name`; otherwise nulls.
+void timing_slot(const char* name, hipEvent_t* start, hipEvent_t* stop);
 
- private:
-  int slot_ = -1;
-  hipStream_t s_;
-};
+// Launches `kernel` on `s`. With timing enabled the start and stop events ride
+// in the kernel's own dispatch (hipExtLaunchKernel), so their elapsed time is
+// the kernel's execution without the gaps around it.
+template <typename... Args, typename F = void (*)(Args...)>
+void launch_kernel(const char* name, F kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  hipEvent_t a = nullptr, b = nullptr;
+  timing_slot(name, &a, &b);
+  if (a)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, a, b, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+}
 
 // Number of compute units of the current device, cached.
 int device_cu_count();

@@ -66,6 +66,121 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ W, 
     if (lane == 0 && t0 + t < ntok) logits[(size_t)(t0 + t) * E + e] = lg[t];
 }
 
+// ------------------------------------------------------------ router, many tokens
+// A workgroup computes a 32-expert x 32-token tile of logits; each thread owns
+// 2 experts x 2 tokens and evaluates each logit on its own, in the same fixed
+// order as the wave router: per 32-block a sequential fp64 sum of the exact
+// fp16 x fp32 products, then the stride-halving tree over the (zero-padded)
+// power-of-two block count. The tree is evaluated depth first: its leaves are
+// visited in bit-reversed order and partial sums are kept per level like the
+// digits of a binary counter (level k holds a sum of 2^k leaves). Operands are
+// staged in LDS as fp64, 4 leaves at a time, converted once per workgroup.
+constexpr int kRtE = 32, kRtT = 32, kRtLeaves = 4;
+constexpr int kRtStride = kRtLeaves * 32 + 2;   // doubles per LDS row (+2: spreads banks)
+constexpr int kRtLevels = 9;                    // up to 256 blocks (hidden <= 8192)
+
+__device__ __forceinline__ int bit_reverse(int v, int bits) {
+  return (int)(__builtin_bitreverse32((uint32_t)v) >> (32 - bits));
+}
+
+__global__ __launch_bounds__(256) void k_router_tiles(const uint16_t* __restrict__ W, const float* __restrict__ x,
+                                                      int ntok, int E, int H, const double* __restrict__ bias,
+                                                      double* __restrict__ logits) {
+  __shared__ double s_w[kRtE][kRtStride];
+  __shared__ double s_x[kRtT][kRtStride];
+  const int tid = threadIdx.x;
+  const int e_base = blockIdx.x * kRtE, t_base = blockIdx.y * kRtT;
+  const int ei = tid >> 4, ti = tid & 15;   // experts ei, ei+16; tokens ti, ti+16
+  const int nb = H >> 5;
+  int L = 0;
+  while ((1 << L) < nb) ++L;
+  const int P2 = 1 << L;
+  // loader mapping: row r (expert or token) = tid >> 3, 16 consecutive values of
+  // one of the chunk's 4 leaves: leaf (tid >> 1) & 3, half tid & 1
+  const int lr = tid >> 3, lk = (tid >> 1) & 3, lh = tid & 1;
+  const int le = min(e_base + lr, E - 1), lt = min(t_base + lr, ntok - 1);
+  double lvl[4][kRtLevels];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int k = 0; k < kRtLevels; ++k) lvl[c][k] = 0.0;
+  for (int i0 = 0; i0 < P2; i0 += kRtLeaves) {
+    {
+      const int b = bit_reverse(i0 + lk, L);
+      double wv[16], xv[16];
+      if (b < nb) {
+        const uint4* wp = reinterpret_cast<const uint4*>(W + (size_t)le * H + (size_t)b * 32 + 16 * lh);
+        const uint4 u0 = wp[0], u1 = wp[1];
+        const uint32_t hw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) wv[j] = (double)half_bits_to_float((hw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+        const float4* xp = reinterpret_cast<const float4*>(x + (size_t)lt * H + (size_t)b * 32 + 16 * lh);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 f = xp[j];
+          xv[4 * j] = f.x; xv[4 * j + 1] = f.y; xv[4 * j + 2] = f.z; xv[4 * j + 3] = f.w;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) wv[j] = xv[j] = 0.0;
+      }
+      __syncthreads();   // the previous chunk's reads are done
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        *reinterpret_cast<double2*>(&s_w[lr][lk * 32 + 16 * lh + j]) = make_double2(wv[j], wv[j + 1]);
+        *reinterpret_cast<double2*>(&s_x[lr][lk * 32 + 16 * lh + j]) = make_double2(xv[j], xv[j + 1]);
+      }
+      __syncthreads();
+    }
+#pragma unroll 1
+    for (int k = 0; k < kRtLeaves; ++k) {
+      const int i = i0 + k;   // depth-first leaf index (uniform)
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+      const bool real = bit_reverse(i, L) < nb;   // padding leaves are +0
+      if (real) {
+#pragma unroll 4
+        for (int j = 0; j < 32; j += 2) {
+          const double2 w0 = *reinterpret_cast<const double2*>(&s_w[ei][k * 32 + j]);
+          const double2 w1 = *reinterpret_cast<const double2*>(&s_w[ei + 16][k * 32 + j]);
+          const double2 x0 = *reinterpret_cast<const double2*>(&s_x[ti][k * 32 + j]);
+          const double2 x1 = *reinterpret_cast<const double2*>(&s_x[ti + 16][k * 32 + j]);
+          acc[0] = fma(w0.x, x0.x, acc[0]); acc[0] = fma(w0.y, x0.y, acc[0]);
+          acc[1] = fma(w0.x, x1.x, acc[1]); acc[1] = fma(w0.y, x1.y, acc[1]);
+          acc[2] = fma(w1.x, x0.x, acc[2]); acc[2] = fma(w1.y, x0.y, acc[2]);
+          acc[3] = fma(w1.x, x1.x, acc[3]); acc[3] = fma(w1.y, x1.y, acc[3]);
+        }
+      }
+      // push the leaf: carry through the occupied levels (bits of i), left + right
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        double carry = acc[c];
+        bool open = true;
+#pragma unroll
+        for (int lv = 0; lv < kRtLevels; ++lv) {
+          if (open) {
+            if ((i >> lv) & 1) {
+              carry = lvl[c][lv] + carry;
+            } else {
+              lvl[c][lv] = carry;
+              open = false;
+            }
+          }
+        }
+      }
+    }
+  }
+  // after P2 = 2^L leaves the whole tree sits at level L
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = e_base + ei + 16 * (c >> 1), t = t_base + ti + 16 * (c & 1);
+    double v = lvl[c][0];
+#pragma unroll
+    for (int lv = 1; lv < kRtLevels; ++lv)
+      if (lv == L) v = lvl[c][lv];
+    if (e < E && t < ntok) logits[(size_t)t * E + e] = bias ? v + bias[e] : v;
+  }
+}
+
 // ------------------------------------------------------------ top-k, one wave per token
 __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits, int ntok, int E, int K,
                                               int32_t* __restrict__ idx, float* __restrict__ gw) {
@@ -172,7 +287,8 @@ int launch_check(const char* what) {
   return QMOE_OK;
 }
 
-KernelTimer::KernelTimer(const char* nm, hipStream_t st) : s_(st) {
+void timing_slot(const char* nm, hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
   if (!g_timing.on) return;
   std::lock_guard<std::mutex> lk(g_timing.mu);
   if (g_timing.used == g_timing.start.size()) {
@@ -182,13 +298,10 @@ KernelTimer::KernelTimer(const char* nm, hipStream_t st) : s_(st) {
     g_timing.stop.push_back(b);
     g_timing.name.emplace_back();
   }
-  slot_ = (int)g_timing.used++;
-  g_timing.name[slot_] = nm;
-  (void)hipEventRecord(g_timing.start[slot_], s_);
-}
-
-KernelTimer::~KernelTimer() {
-  if (slot_ >= 0) (void)hipEventRecord(g_timing.stop[slot_], s_);
+  const size_t slot = g_timing.used++;
+  g_timing.name[slot] = nm;
+  *start = g_timing.start[slot];
+  *stop = g_timing.stop[slot];
 }
 
 int device_cu_count() {
@@ -230,8 +343,7 @@ int launch_quant(const float* x, int64_t nblocks, int rot, int8_t* xq, float* dx
   if (nblocks == 0) return QMOE_OK;
   const int threads = 256;
   const unsigned grid = (unsigned)((nblocks + threads - 1) / threads);
-  KernelTimer kt("quant_act", s);
-  hipLaunchKernelGGL(k_quant_act, dim3(grid), dim3(threads), 0, s, x, nblocks, rot, xq, dx);
+  launch_kernel("quant_act", k_quant_act, dim3(grid), dim3(threads), s, x, nblocks, rot, xq, dx);
   return launch_check("quant_act");
 }
 
@@ -239,18 +351,20 @@ int launch_route(const qmoe_layer* L, const float* x, int32_t ntok, double* logi
                  hipStream_t s) {
   if (L->hidden > 32 * 64 * kRouterMaxC)
     QMOE_FAIL(QMOE_E_SHAPE, "hidden=%d exceeds router limit %d", L->hidden, 32 * 64 * kRouterMaxC);
-  {
+  if (ntok >= kRtT / 2) {   // many tokens: 32 x 32 logit tiles (same order, same bits)
+    dim3 grid((L->n_experts + kRtE - 1) / kRtE, (ntok + kRtT - 1) / kRtT);
+    launch_kernel("router", k_router_tiles, grid, dim3(256), s, L->w_router, x, ntok, L->n_experts, L->hidden,
+                  L->router_bias, logits);
+  } else {
     dim3 grid((L->n_experts + 3) / 4, (ntok + 3) / 4);
-    KernelTimer kt("router", s);
-    hipLaunchKernelGGL(k_router, grid, dim3(256), 0, s, L->w_router, x, ntok, L->n_experts, L->hidden,
-                       L->router_bias, logits);
+    launch_kernel("router", k_router, grid, dim3(256), s, L->w_router, x, ntok, L->n_experts, L->hidden,
+                  L->router_bias, logits);
   }
   int st = launch_check("router");
   if (st) return st;
   {
     dim3 grid((ntok + 3) / 4);
-    KernelTimer kt("topk", s);
-    hipLaunchKernelGGL(k_topk, grid, dim3(256), 0, s, logits, ntok, L->n_experts, L->topk, idx, gw);
+    launch_kernel("topk", k_topk, grid, dim3(256), s, logits, ntok, L->n_experts, L->topk, idx, gw);
   }
   return launch_check("topk");
 }
@@ -264,8 +378,7 @@ void launch_matvec_t(const uint8_t* W, int64_t rows, size_t row_bytes, int nb, i
                      const int8_t* xq, const float* dx, float* y, hipStream_t s) {
   const int rows_per_wg = 4 * (64 >> lpr_log2);
   const unsigned grid = (unsigned)((rows + rows_per_wg - 1) / rows_per_wg);
-  KernelTimer kt("matvec", s);
-  hipLaunchKernelGGL((k_matvec<FMT, Q>), dim3(grid), dim3(256), 0, s, W, rows, row_bytes, nb, lpr_log2, cb, xq, dx, y);
+  launch_kernel("matvec", k_matvec<FMT, Q>, dim3(grid), dim3(256), s, W, rows, row_bytes, nb, lpr_log2, cb, xq, dx, y);
 }
 
 template <int FMT>

@@ -397,15 +397,15 @@ __global__ __launch_bounds__(256) void k_gateup(PrefillArgs a) {
     for (int n = 0; n < 4; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[m][n][r] = 0.0f;
+  // the next stage's loads are in flight while the current stage is multiplied
   const int nst = a.nb_h / kKB;
+  StageLoader<FMT, 2> L;
+  L.load(wg, wu, a.gu_row_bytes, a.nb_h, row0, 0, arow, adrow);
   for (int st = 0; st < nst; ++st) {
-    {
-      StageLoader<FMT, 2> L;
-      L.load(wg, wu, a.gu_row_bytes, a.nb_h, row0, st * kKB, arow, adrow);
-      __syncthreads();               // the previous stage's LDS reads are done
-      L.store(S);
-    }
+    __syncthreads();                 // the previous stage's LDS reads are done
+    L.store(S);
     __syncthreads();
+    L.load(wg, wu, a.gu_row_bytes, a.nb_h, row0, min(st + 1, nst - 1) * kKB, arow, adrow);   // last: a reload
     stage_mma<FMT, 2>(S, cb, acc);
   }
   // SwiGLU into LDS as [pair][row] (reusing the activation stage buffer), then
@@ -464,14 +464,13 @@ __global__ __launch_bounds__(256) void k_down(PrefillArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[0][n][r] = 0.0f;
   const int nst = a.nb_i / kKB;
+  StageLoader<FMT, 1> L;
+  L.load(wd, wd, a.dn_row_bytes, a.nb_i, row0, 0, arow, adrow);
   for (int st = 0; st < nst; ++st) {
-    {
-      StageLoader<FMT, 1> L;
-      L.load(wd, wd, a.dn_row_bytes, a.nb_i, row0, st * kKB, arow, adrow);
-      __syncthreads();
-      L.store(S);
-    }
     __syncthreads();
+    L.store(S);
+    __syncthreads();
+    L.load(wd, wd, a.dn_row_bytes, a.nb_i, row0, min(st + 1, nst - 1) * kKB, arow, adrow);
     stage_mma<FMT, 1>(S, cb, acc);
   }
   const int i16 = lane & 15, q = lane >> 4;
@@ -510,21 +509,18 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ypair
 template <int FG, int FD>
 int launch_gemms(const PrefillArgs& a, int tiles_max, int ntok, float* out, hipStream_t s) {
   {
-    KernelTimer kt("gateup_mfma", s);
-    hipLaunchKernelGGL((k_gateup<FG>), dim3(tiles_max, a.inter / kTileM), dim3(256), 0, s, a);
+    launch_kernel("gateup_mfma", k_gateup<FG>, dim3(tiles_max, a.inter / kTileM), dim3(256), s, a);
   }
   int st = launch_check("gateup_mfma");
   if (st) return st;
   {
-    KernelTimer kt("down_mfma", s);
-    hipLaunchKernelGGL((k_down<FD>), dim3(tiles_max, a.hidden / kTileM), dim3(256), 0, s, a);
+    launch_kernel("down_mfma", k_down<FD>, dim3(tiles_max, a.hidden / kTileM), dim3(256), s, a);
   }
   if ((st = launch_check("down_mfma"))) return st;
   {
     const size_t n4 = (size_t)ntok * a.hidden / 4;
     const unsigned grid = (unsigned)std::min<size_t>((n4 + 255) / 256, 8192);
-    KernelTimer kt("combine", s);
-    hipLaunchKernelGGL(k_combine, dim3(grid), dim3(256), 0, s, a.ypair, ntok, a.K, a.hidden, out);
+    launch_kernel("combine", k_combine, dim3(grid), dim3(256), s, a.ypair, ntok, a.K, a.hidden, out);
   }
   return launch_check("combine");
 }
@@ -559,10 +555,11 @@ extern "C" int qmoe_prefill_layer(const qmoe_layer* L, const float* x, int32_t n
   if ((st = launch_route(L, x, ntok, w.logits, w.idx, w.gw, s))) return st;
   GroupPtrs g = group_ptrs(w.group, E, npairs);
   {
-    KernelTimer kt("group", s);
-    hipLaunchKernelGGL(k_count, dim3(E), dim3(256), 0, s, w.idx, npairs, g.counts);
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(512), 0, s, g.counts, E, npairs, g.offsets, g.ntiles, g.tiles);
-    hipLaunchKernelGGL(k_scatter, dim3(E), dim3(256), 0, s, w.idx, npairs, g.offsets, g.pairs);
+    launch_kernel("group_count", k_count, dim3(E), dim3(256), s, (const int32_t*)w.idx, npairs, g.counts);
+    launch_kernel("group_scan", k_scan, dim3(1), dim3(512), s, (const int32_t*)g.counts, E, npairs, g.offsets, g.ntiles,
+                  g.tiles);
+    launch_kernel("group_scatter", k_scatter, dim3(E), dim3(256), s, (const int32_t*)w.idx, npairs,
+                  (const int32_t*)g.offsets, g.pairs);
   }
   if ((st = launch_check("group"))) return st;
   FormatInfo fg, fd;

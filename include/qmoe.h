@@ -187,11 +187,14 @@ typedef struct {
 int qmoe_workspace_layout(const qmoe_layer* L, int32_t max_tokens, qmoe_ws_layout* out);
 
 /* Kernel timing (instrumentation). qmoe_timing_enable(1) starts recording, for
- * every kernel that an entry point launches afterwards, a pair of HIP events on
- * the call's stream; (0) stops; either call discards earlier records.
- * qmoe_timing_read waits for the recorded kernels named `name` ("quant_act",
- * "router", "topk", "gateup", "down", "matvec", "group", "gateup_mfma",
- * "down_mfma", "combine") and returns their summed time in ms and their count. */
+ * every kernel that an entry point launches afterwards, a pair of HIP events
+ * carried by the kernel's own dispatch (so the elapsed time is the kernel's
+ * execution); (0) stops; either call discards earlier records.
+ * qmoe_timing_read waits for the recorded kernels named `name` and returns
+ * their summed time in ms and their count. Names: "quant_act", "router",
+ * "topk", "matvec" (shared); "route", "gateup", "down" (decode);
+ * "group_count", "group_scan", "group_scatter", "gateup_mfma", "down_mfma",
+ * "combine" (prefill). */
 int qmoe_timing_enable(int on);
 int qmoe_timing_read(const char* name, double* total_ms, int* count);
 

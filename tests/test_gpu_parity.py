@@ -201,6 +201,47 @@ def test_route_expert_counts(E):
     assert moe.rel_l2(out, ref) < TOL
 
 
+@pytest.mark.parametrize("ntok", [3, 40])
+def test_route_hidden_8192(ntok):
+    """The largest hidden size (256 blocks per row: three in-lane tree levels in
+    the wave router, nine levels in the tiled router) stays bit-exact."""
+    spec = gen.LayerSpec.tiny(hidden=8192, n_experts=8, topk=2)
+    dl = qm.device.DeviceLayer(spec, seed=14)
+    x = gen.tokens(ntok, spec.hidden, seed=14)
+    ws = dl.workspace(ntok)
+    idx = torch.empty((ntok, spec.topk), dtype=torch.int32, device="cuda")
+    gw = torch.empty((ntok, spec.topk), dtype=torch.float32, device="cuda")
+    qm.qmoe_route(dl.desc, dev(x), idx, gw, ws)
+    torch.cuda.synchronize()
+    lay = qm.qmoe_workspace_layout(dl.desc, ntok)
+    lg = ws[lay["logits"]: lay["logits"] + ntok * 8 * 8].cpu().numpy().view(np.float64).reshape(ntok, 8)
+    assert np.array_equal(lg, router.logits(dl.w_router_host, x))
+    if ntok == 3:
+        out, _ = run_decode(dl, x[:1])
+        ref, _, _ = moe.moe_tokens(oracle_layer(spec, 14, dl.w_router_host), x[:1])
+        assert moe.rel_l2(out, ref) < TOL
+
+
+@pytest.mark.parametrize("ntok,E,hidden", [(16, 40, 256), (100, 256, 768), (33, 300, 512), (64, 512, 1024)])
+def test_route_tiled_logits_bit_exact(ntok, E, hidden):
+    """The many-token router (32 x 32 logit tiles, depth-first tree) gives the
+    oracle's fp64 logits bit for bit, ragged expert and token tiles included."""
+    spec = gen.LayerSpec.tiny(hidden=hidden, n_experts=E, topk=8)
+    bias = gen.zipf_bias(E)
+    dl = qm.device.DeviceLayer(spec, seed=15, bias=bias)
+    x = gen.tokens(ntok, spec.hidden, seed=15)
+    ws = dl.workspace(ntok)
+    idx = torch.empty((ntok, spec.topk), dtype=torch.int32, device="cuda")
+    gw = torch.empty((ntok, spec.topk), dtype=torch.float32, device="cuda")
+    qm.qmoe_route(dl.desc, dev(x), idx, gw, ws)
+    torch.cuda.synchronize()
+    lay = qm.qmoe_workspace_layout(dl.desc, ntok)
+    lg = ws[lay["logits"]: lay["logits"] + ntok * E * 8].cpu().numpy().view(np.float64).reshape(ntok, E)
+    assert np.array_equal(lg, router.logits(dl.w_router_host, x, bias))
+    idx_ref, _, _ = router.route(dl.w_router_host, x, bias, spec.topk)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+
+
 # ------------------------------------------------------------------ decode layer
 
 def run_decode(dl, x, ws=None):

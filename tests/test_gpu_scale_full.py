@@ -113,3 +113,57 @@ def test_dense_mix(ncols):
         err = moe.rel_l2(y.cpu().numpy(), y_ref)
         print(f"dense FP{c.fmt} {c.rows}x{c.k} rot={c.rot} ncols={ncols}: rel_l2 {err:.2e}")
         assert err < TOL
+
+
+def test_full_prefill_8k_zipf(full):
+    """8192 tokens with Zipf-biased routing (the benchmark's prefill input):
+    grouping invariants over all pairs, routing bit-exact on a 256-token sample,
+    sampled tokens (first, last, one through the hottest and one through the
+    rarest expert) against the per-token oracle, and a bit-identical repeat."""
+    spec, dl, _ = full
+    T = 8192
+    bias = gen.zipf_bias(spec.n_experts)
+    bias_d = torch.from_numpy(bias).cuda()
+    desc = qm.make_layer(spec.hidden, spec.inter, spec.n_experts, spec.topk, spec.fmt_gate, spec.fmt_up,
+                         spec.fmt_down, 0, 0, dl.w_router, bias_d, dl.gate, dl.up, dl.down, dl.cb_gate, dl.cb_up,
+                         dl.cb_down)
+    x = gen.tokens(T, spec.hidden, seed=SEED, stream=9)
+    xd = qm.device.to_device(x)
+    out = torch.empty_like(xd)
+    ws = torch.zeros(qm.qmoe_workspace_bytes(desc, T), dtype=torch.uint8, device="cuda")
+    qm.qmoe_prefill_layer(desc, xd, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    lay = qm.qmoe_workspace_layout(desc, T)
+    K, E = spec.topk, spec.n_experts
+    idx = ws[lay["idx"]: lay["idx"] + 4 * T * K].cpu().numpy().view(np.int32).reshape(T, K)
+    grp = ws[lay["group"]: lay["group"] + 4 * (3 * E + 1 + T * K)].cpu().numpy().view(np.int32)
+    counts, offsets, pairs = grp[:E], grp[E:2 * E + 1], grp[3 * E + 1:]
+    assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=E))
+    assert offsets[0] == 0 and offsets[E] == T * K and np.array_equal(np.diff(offsets), counts)
+    for e in range(E):                                  # each expert's pairs, ascending
+        seg = pairs[offsets[e]: offsets[e + 1]]
+        assert np.all(idx.ravel()[seg] == e) and np.all(np.diff(seg) > 0)
+    sample = np.arange(0, T, 32)
+    idx_ref, _, _ = router.route(dl.w_router_host, x[sample], bias, K)
+    assert np.array_equal(idx[sample], idx_ref)
+    hot = int(np.argmax(counts))
+    live = np.nonzero(counts)[0]
+    rare = int(live[np.argmin(counts[live])])
+    picks = [0, T - 1, int(np.nonzero((idx == hot).any(1))[0][5]), int(np.nonzero((idx == rare).any(1))[0][0])]
+    cache = {}
+
+    def get(name, e):
+        if (name, e) not in cache:
+            t = gen.expert_tensor(spec, name, e, SEED)
+            cache[(name, e)] = (t.fmt, t.codes, t.scales, t.cb)
+        return cache[(name, e)]
+
+    Lb = moe.Layer(spec.hidden, spec.inter, E, K, dl.w_router_host, get, bias)
+    ref, _, _ = moe.moe_tokens(Lb, x[picks])
+    for i, t in enumerate(picks):
+        assert moe.rel_l2(got[t], ref[i]) < TOL, (t, moe.rel_l2(got[t], ref[i]))
+    qm.qmoe_prefill_layer(desc, xd, out, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), got)
