@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="only the q=1 headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="before the benchmark, copy MIB MiB device-to-device once (a plain copy of known size, "
+                         "for scaling memory-traffic counters)")
+    ap.add_argument("--prefill-only", action="store_true", help="only the 8K-token prefill (for profiling)")
     return ap.parse_args()
 
 
@@ -91,12 +95,25 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     spec = gen.LayerSpec.full()
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} bytes read + {n} bytes written")
+        del src, dst
     t0 = time.time()
     dl = qm.device.DeviceLayer(spec, seed=0)
     per_expert = dl.packed_bytes_per_expert()
     log(f"built full layer ({per_expert * spec.n_experts:,} packed bytes) in {time.time() - t0:.1f}s")
     gateup_bytes = qm.qmoe_packed_bytes(2, spec.inter, spec.hidden) * 2
     down_bytes = qm.qmoe_packed_bytes(3, spec.hidden, spec.inter)
+    if args.prefill_only:
+        res = bench_prefill(torch, qm, gen, spec, dl, dev)
+        print(json.dumps({"prefill_8k": res}), flush=True)
+        return
     ws = dl.workspace(4)
     toks = torch.from_numpy(gen.tokens(64, spec.hidden, seed=0, stream=7)).to(dev)
     out = torch.empty((4, spec.hidden), dtype=torch.float32, device=dev)

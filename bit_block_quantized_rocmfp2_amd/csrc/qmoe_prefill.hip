@@ -362,10 +362,15 @@ struct TileInfo {
   int e, first, cnt, pbase;
 };
 
+// Grid: x = 64-row weight tile, y = pair tile. Workgroups are dispatched in x-
+// fastest order and spread over the 8 XCDs by id modulo 8: all row tiles of one
+// pair tile run close together (its activations are fetched once per XCD), and
+// when the row-tile count is a multiple of 8 (32 and 64 for inter 2048 and
+// hidden 4096) each row tile's weights stay on one XCD for every pair tile.
 __device__ __forceinline__ bool tile_info(const PrefillArgs& a, TileInfo& t) {
-  if ((int)blockIdx.x >= *a.ntiles) return false;
-  t.e = a.tiles[2 * blockIdx.x];
-  t.first = a.tiles[2 * blockIdx.x + 1];
+  if ((int)blockIdx.y >= *a.ntiles) return false;
+  t.e = a.tiles[2 * blockIdx.y];
+  t.first = a.tiles[2 * blockIdx.y + 1];
   t.cnt = min(kTileN, a.counts[t.e] - t.first);
   t.pbase = a.offsets[t.e] + t.first;
   return true;
@@ -379,7 +384,7 @@ __global__ __launch_bounds__(256) void k_gateup(PrefillArgs a) {
   __shared__ StageLds<FMT, 2> S;
   __shared__ int s_pair[kTileN];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int row0 = blockIdx.y * kTileM;
+  const int row0 = blockIdx.x * kTileM;
   if (tid < kTileN) s_pair[tid] = a.pairs[T.pbase + min(tid, T.cnt - 1)];   // padding repeats a valid pair
   __syncthreads();
   // the token rows this thread loads (pair tid >> 2 for bytes, tid >> 1 for scales)
@@ -449,7 +454,7 @@ __global__ __launch_bounds__(256) void k_down(PrefillArgs a) {
   __shared__ StageLds<FMT, 1> S;
   __shared__ int s_pair[kTileN];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int row0 = blockIdx.y * kTileM;
+  const int row0 = blockIdx.x * kTileM;
   if (tid < kTileN) s_pair[tid] = a.pairs[T.pbase + min(tid, T.cnt - 1)];
   __syncthreads();
   // hq / dh rows are indexed by the pair's sorted position (padding repeats the last)
@@ -509,12 +514,12 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ypair
 template <int FG, int FD>
 int launch_gemms(const PrefillArgs& a, int tiles_max, int ntok, float* out, hipStream_t s) {
   {
-    launch_kernel("gateup_mfma", k_gateup<FG>, dim3(tiles_max, a.inter / kTileM), dim3(256), s, a);
+    launch_kernel("gateup_mfma", k_gateup<FG>, dim3(a.inter / kTileM, tiles_max), dim3(256), s, a);
   }
   int st = launch_check("gateup_mfma");
   if (st) return st;
   {
-    launch_kernel("down_mfma", k_down<FD>, dim3(tiles_max, a.hidden / kTileM), dim3(256), s, a);
+    launch_kernel("down_mfma", k_down<FD>, dim3(a.hidden / kTileM, tiles_max), dim3(256), s, a);
   }
   if ((st = launch_check("down_mfma"))) return st;
   {
