@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="only the q=1 headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=8)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before the benchmark, copy MIB MiB device-to-device once (a plain copy of known size, "
                          "for scaling memory-traffic counters)")
@@ -307,9 +307,11 @@ def cpu_baseline(args, spec, dl, per_expert):
             cache[(name, int(e))] = (t.fmt, t.codes, t.scales, t.cb)
     L = moe.Layer(spec.hidden, spec.inter, spec.n_experts, spec.topk, dl.w_router_host,
                   lambda nm, e: cache[(nm, e)])
-    t0 = time.perf_counter()
-    moe.moe_tokens(L, x)
-    dt = time.perf_counter() - t0
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):   # the stated core count: one thread, BLAS included
+        t0 = time.perf_counter()
+        moe.moe_tokens(L, x)
+        dt = time.perf_counter() - t0
     gbs = n * spec.topk * per_expert / dt / 1e9
     log(f"cpu oracle: {n} tokens in {dt:.1f}s -> {gbs:.4f} GB/s effective")
     return {"value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
