@@ -24,6 +24,11 @@ namespace qk {
 
 constexpr int kWave = 64;
 
+// Native vector types for wide loads: unlike HIP's uint4 / uint2 classes they stay
+// in registers when held across loops and barriers.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   // v_perm_b32: result byte i = byte sel_i of the 8-byte value {hi, lo} (lo = bytes 0..3)
   return __builtin_amdgcn_perm(hi, lo, sel);
@@ -69,26 +74,26 @@ struct Blocks {
     constexpr int LW = Fmt<FMT>::kLoWords;
     const uint8_t* codes = row + (size_t)b * LW * 4;
     if constexpr (LW * NBL == 4) {
-      uint4 v = *reinterpret_cast<const uint4*>(codes);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(codes);
       uint32_t t[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int i = 0; i < NBL; ++i)
 #pragma unroll
         for (int w = 0; w < LW; ++w) lo[i][w] = t[i * LW + w];
     } else if constexpr (LW * NBL == 2) {
-      uint2 v = *reinterpret_cast<const uint2*>(codes);
+      const u32x2 v = *reinterpret_cast<const u32x2*>(codes);
       lo[0][0] = v.x;
       lo[0][1] = v.y;
     } else {  // FP4, NBL = 2: 32 bytes
-      uint4 v0 = *reinterpret_cast<const uint4*>(codes);
-      uint4 v1 = *reinterpret_cast<const uint4*>(codes + 16);
+      const u32x4 v0 = *reinterpret_cast<const u32x4*>(codes);
+      const u32x4 v1 = *reinterpret_cast<const u32x4*>(codes + 16);
       lo[0][0] = v0.x; lo[0][1] = v0.y; lo[0][2] = v0.z; lo[0][3] = v0.w;
       lo[NBL - 1][0] = v1.x; lo[NBL - 1][1] = v1.y; lo[NBL - 1][2] = v1.z; lo[NBL - 1][3] = v1.w;
     }
     const uint8_t* after_lo = row + (size_t)nb * LW * 4;
     if constexpr (Fmt<FMT>::kHi) {
       if constexpr (NBL == 2) {
-        uint2 h = *reinterpret_cast<const uint2*>(after_lo + (size_t)b * 4);
+        const u32x2 h = *reinterpret_cast<const u32x2*>(after_lo + (size_t)b * 4);
         hi[0] = h.x;
         hi[NBL - 1] = h.y;
       } else {
@@ -156,8 +161,8 @@ struct Acts {
   __device__ __forceinline__ void load(const int8_t* xq, const float* dx, int b) {
 #pragma unroll
     for (int i = 0; i < NBL; ++i) {
-      const uint4* p = reinterpret_cast<const uint4*>(xq + (size_t)(b + i) * 32);
-      uint4 a = p[0], c = p[1];
+      const u32x4* p = reinterpret_cast<const u32x4*>(xq + (size_t)(b + i) * 32);
+      const u32x4 a = p[0], c = p[1];
       q[i][0] = a.x; q[i][1] = a.y; q[i][2] = a.z; q[i][3] = a.w;
       q[i][4] = c.x; q[i][5] = c.y; q[i][6] = c.z; q[i][7] = c.w;
       d[i] = dx[b + i];
@@ -323,11 +328,11 @@ __device__ __forceinline__ void router_wave(const uint16_t* __restrict__ W, cons
   for (int c = 0; c < kRouterMaxC; ++c) {
     const int b = lane + 64 * c;
     if (c < C && b < nb) {
-      const uint4* wp = reinterpret_cast<const uint4*>(W + (size_t)e * H + (size_t)b * 32);
+      const u32x4* wp = reinterpret_cast<const u32x4*>(W + (size_t)e * H + (size_t)b * 32);
       uint32_t wv[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        uint4 u = wp[i];
+        const u32x4 u = wp[i];
         wv[4 * i] = u.x; wv[4 * i + 1] = u.y; wv[4 * i + 2] = u.z; wv[4 * i + 3] = u.w;
       }
 #pragma unroll

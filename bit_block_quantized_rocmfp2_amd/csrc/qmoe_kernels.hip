@@ -109,8 +109,8 @@ __global__ __launch_bounds__(256) void k_router_tiles(const uint16_t* __restrict
       const int b = bit_reverse(i0 + lk, L);
       double wv[16], xv[16];
       if (b < nb) {
-        const uint4* wp = reinterpret_cast<const uint4*>(W + (size_t)le * H + (size_t)b * 32 + 16 * lh);
-        const uint4 u0 = wp[0], u1 = wp[1];
+        const u32x4* wp = reinterpret_cast<const u32x4*>(W + (size_t)le * H + (size_t)b * 32 + 16 * lh);
+        const u32x4 u0 = wp[0], u1 = wp[1];
         const uint32_t hw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
         for (int j = 0; j < 16; ++j) wv[j] = (double)half_bits_to_float((hw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
@@ -257,8 +257,8 @@ __global__ __launch_bounds__(256) void k_block_dots(const uint8_t* __restrict__ 
   load_codebook<FMT>(cbp, cb);
   Blocks<FMT, 1> bl;
   bl.load(W + (size_t)r * row_bytes, nb, b);
-  const uint4* p = reinterpret_cast<const uint4*>(xq + (size_t)b * 32);
-  uint4 a = p[0], c = p[1];
+  const u32x4* p = reinterpret_cast<const u32x4*>(xq + (size_t)b * 32);
+  const u32x4 a = p[0], c = p[1];
   const uint32_t x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
   uint32_t w[8];
   bl.expand(0, cb, w);

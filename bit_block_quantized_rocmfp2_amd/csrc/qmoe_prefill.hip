@@ -40,8 +40,6 @@ using namespace qmoe;
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTileN = 64;   // pairs (tokens) per tile
 constexpr int kTileM = 64;   // weight rows per workgroup
@@ -297,13 +295,13 @@ struct StageLoader {
   }
 };
 
-// Multiply one stage: wave w owns rows 16w..16w+15 of each matrix and all 64
-// pairs (four 16-column MFMA tiles). acc[m][n][r] accumulates row 16w + 4q + r,
+// Multiply one stage: wave w owns rows 16w..16w+15 of each matrix and the
+// tile's pairs as up to four 16-column MFMA tiles (nn of them hold pairs). acc[m][n][r] accumulates row 16w + 4q + r,
 // column 16n + l % 16 (q = l / 16), in fp32: per block, the int32 MFMA result
 // times (weight scale x activation scale).
 template <int FMT, int NMAT>
 __device__ __forceinline__ void stage_mma(const StageLds<FMT, NMAT>& S, const uint32_t cb[NMAT][4],
-                                          float acc[NMAT][4][4]) {
+                                          float acc[NMAT][4][4], int nn) {
   constexpr int LW = Fmt<FMT>::kLoWords;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i16 = lane & 15, q = lane >> 4;
@@ -320,6 +318,7 @@ __device__ __forceinline__ void stage_mma(const StageLds<FMT, NMAT>& S, const ui
     for (int m = 0; m < NMAT; ++m) sw[m] = *reinterpret_cast<const float4*>(&S.s[m][b][rd]);
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
+      if (n < nn) {   // 16-column subtiles beyond the tile's pairs are skipped (uniform)
       const int col = 16 * n + i16;
       const long B = *reinterpret_cast<const long*>(&S.x[col][b * 8 + 2 * q]);
       const float d = S.dx[b][col];
@@ -330,6 +329,7 @@ __device__ __forceinline__ void stage_mma(const StageLds<FMT, NMAT>& S, const ui
         acc[m][n][1] = fmaf((float)P[1], sw[m].y * d, acc[m][n][1]);
         acc[m][n][2] = fmaf((float)P[2], sw[m].z * d, acc[m][n][2]);
         acc[m][n][3] = fmaf((float)P[3], sw[m].w * d, acc[m][n][3]);
+      }
       }
     }
   }
@@ -386,6 +386,7 @@ __global__ __launch_bounds__(256) void k_gateup(PrefillArgs a) {
   __shared__ int s_pair[kTileN];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row0 = blockIdx.x * kTileM;
+  const int nn = (T.cnt + 15) >> 4;   // 16-column subtiles holding pairs
   if (tid < kTileN) s_pair[tid] = a.pairs[T.pbase + min(tid, T.cnt - 1)];   // padding repeats a valid pair
   __syncthreads();
   // the token rows this thread loads (pair tid >> 2 for bytes, tid >> 1 for scales)
@@ -403,16 +404,18 @@ __global__ __launch_bounds__(256) void k_gateup(PrefillArgs a) {
     for (int n = 0; n < 4; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[m][n][r] = 0.0f;
-  // the next stage's loads are in flight while the current stage is multiplied
+  // two weight matrices leave no registers for a prefetch at four waves per SIMD:
+  // each stage is loaded, stored to LDS and multiplied (other workgroups overlap)
   const int nst = a.nb_h / kKB;
-  StageLoader<FMT, 2> L;
-  L.load(wg, wu, a.gu_row_bytes, a.nb_h, row0, 0, arow, adrow);
   for (int st = 0; st < nst; ++st) {
-    __syncthreads();                 // the previous stage's LDS reads are done
-    L.store(S);
+    {
+      StageLoader<FMT, 2> L;
+      L.load(wg, wu, a.gu_row_bytes, a.nb_h, row0, st * kKB, arow, adrow);
+      __syncthreads();               // the previous stage's LDS reads are done
+      L.store(S);
+    }
     __syncthreads();
-    L.load(wg, wu, a.gu_row_bytes, a.nb_h, row0, min(st + 1, nst - 1) * kKB, arow, adrow);   // last: a reload
-    stage_mma<FMT, 2>(S, cb, acc);
+    stage_mma<FMT, 2>(S, cb, acc, nn);
   }
   // SwiGLU into LDS as [pair][row] (reusing the activation stage buffer), then
   // requantize each (pair, 32-row block).
@@ -448,36 +451,46 @@ __global__ __launch_bounds__(256) void k_gateup(PrefillArgs a) {
 }
 
 // ------------------------------------------------------------ k_down
+// A workgroup covers 128 rows as two 64-row halves multiplied like the gate and
+// up matrices of k_gateup, so each activation operand read from LDS feeds twice
+// the MFMAs.
 template <int FMT>
 __global__ __launch_bounds__(256) void k_down(PrefillArgs a) {
   TileInfo T;
   if (!tile_info(a, T)) return;
-  __shared__ StageLds<FMT, 1> S;
+  __shared__ StageLds<FMT, 2> S;
   __shared__ int s_pair[kTileN];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int row0 = blockIdx.x * kTileM;
+  const int row0 = blockIdx.x * 2 * kTileM;
+  const int nn = (T.cnt + 15) >> 4;
   if (tid < kTileN) s_pair[tid] = a.pairs[T.pbase + min(tid, T.cnt - 1)];
   __syncthreads();
   // hq / dh rows are indexed by the pair's sorted position (padding repeats the last)
   const int8_t* arow = a.hq + (size_t)(T.pbase + min(tid >> 2, T.cnt - 1)) * a.inter;
   const float* adrow = a.dh + (size_t)(T.pbase + min((tid >> 1) & (kTileN - 1), T.cnt - 1)) * a.nb_i;
   const uint8_t* wd = a.down + (size_t)T.e * a.dn_stride;
-  uint32_t cb[1][4];
+  const uint8_t* wd_hi = wd + (size_t)kTileM * a.dn_row_bytes;   // the second 64-row half
+  uint32_t cb[2][4];
   load_codebook<FMT>(a.cb_down + ((size_t)T.e << FMT), cb[0]);
-  float acc[1][4][4];
 #pragma unroll
-  for (int n = 0; n < 4; ++n)
+  for (int i = 0; i < 4; ++i) cb[1][i] = cb[0][i];
+  float acc[2][4][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[0][n][r] = 0.0f;
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[m][n][r] = 0.0f;
   const int nst = a.nb_i / kKB;
-  StageLoader<FMT, 1> L;
-  L.load(wd, wd, a.dn_row_bytes, a.nb_i, row0, 0, arow, adrow);
   for (int st = 0; st < nst; ++st) {
+    {
+      StageLoader<FMT, 2> L;
+      L.load(wd, wd_hi, a.dn_row_bytes, a.nb_i, row0, st * kKB, arow, adrow);
+      __syncthreads();
+      L.store(S);
+    }
     __syncthreads();
-    L.store(S);
-    __syncthreads();
-    L.load(wd, wd, a.dn_row_bytes, a.nb_i, row0, min(st + 1, nst - 1) * kKB, arow, adrow);
-    stage_mma<FMT, 1>(S, cb, acc);
+    stage_mma<FMT, 2>(S, cb, acc, nn);
   }
   const int i16 = lane & 15, q = lane >> 4;
 #pragma unroll
@@ -486,8 +499,11 @@ __global__ __launch_bounds__(256) void k_down(PrefillArgs a) {
     if (j < T.cnt) {
       const int pair = s_pair[j];
       const float g = a.gw[pair];
-      const float4 v = make_float4(acc[0][n][0] * g, acc[0][n][1] * g, acc[0][n][2] * g, acc[0][n][3] * g);
-      *reinterpret_cast<float4*>(a.ypair + (size_t)pair * a.hidden + row0 + 16 * wave + 4 * q) = v;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const float4 v = make_float4(acc[m][n][0] * g, acc[m][n][1] * g, acc[m][n][2] * g, acc[m][n][3] * g);
+        *reinterpret_cast<float4*>(a.ypair + (size_t)pair * a.hidden + row0 + kTileM * m + 16 * wave + 4 * q) = v;
+      }
     }
   }
 }
@@ -520,7 +536,7 @@ int launch_gemms(const PrefillArgs& a, int tiles_max, int ntok, float* out, hipS
   int st = launch_check("gateup_mfma");
   if (st) return st;
   {
-    launch_kernel("down_mfma", k_down<FD>, dim3(a.hidden / kTileM, tiles_max), dim3(256), s, a);
+    launch_kernel("down_mfma", k_down<FD>, dim3(a.hidden / (2 * kTileM), tiles_max), dim3(256), s, a);
   }
   if ((st = launch_check("down_mfma"))) return st;
   {
@@ -551,7 +567,7 @@ extern "C" int qmoe_prefill_layer(const qmoe_layer* L, const float* x, int32_t n
   if (!x || !out) QMOE_FAIL(QMOE_E_INVAL, "NULL pointer");
   if (!aligned16(x) || !aligned16(out)) QMOE_FAIL(QMOE_E_INVAL, "x / out not 16-byte aligned");
   // tile shapes: rows in 64s, K in stages of 8 blocks (guaranteed by the 16-byte row rule)
-  if (L->inter % kTileM || L->hidden % kTileM || (L->hidden / 32) % kKB || (L->inter / 32) % kKB)
+  if (L->inter % kTileM || L->hidden % (2 * kTileM) || (L->hidden / 32) % kKB || (L->inter / 32) % kKB)
     QMOE_FAIL(QMOE_E_SHAPE, "prefill needs hidden and inter multiples of 256 (hidden=%d inter=%d)", L->hidden,
               L->inter);
   hipStream_t s = as_stream(stream);
