@@ -15,9 +15,8 @@
 //     fits on AMD Strix Halo" (gate/up 2.5 bpw, down 3.5 bpw, per-expert
 //     codebooks).
 //
-//   k_route    one single-wave workgroup per expert: fp64 logits of the q
-//              tokens; the workgroups also share the int8 quantization of the
-//              tokens.
+//   k_route    one workgroup per expert, one wave per token: fp64 logits; the
+//              workgroups also share the int8 quantization of the tokens.
 //   k_gateup   one workgroup per (planned expert slot, 32 rows). Every
 //              workgroup first selects the top-k of each token from the logits
 //              and builds the plan itself (the union of the chosen experts in
@@ -76,21 +75,18 @@ struct DecodeArgs {
 
 // ------------------------------------------------------------ k_route
 template <int Q>
-__global__ __launch_bounds__(64) void k_route(DecodeArgs a) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(64 * Q) void k_route(DecodeArgs a) {
+  // wave t computes expert e's logit for token t (one wave per token)
+  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
   const int e = blockIdx.x;
-  double lg[Q];
-  router_wave<Q>(a.w_router, a.x, a.q, a.hidden, a.bias, e, 0, lane, lg);
-  double mine = lg[0];   // lane t writes token t
-#pragma unroll
-  for (int t = 1; t < Q; ++t)
-    if (lane == t) mine = lg[t];
-  if (lane < a.q) a.logits[(size_t)lane * a.E + e] = mine;
-  // this workgroup's share of the int8 token quantization
+  double lg[1];
+  router_wave<1>(a.w_router, a.x + (size_t)t * a.hidden, 1, a.hidden, a.bias, e, 0, lane, lg);
+  if (lane == 0 && t < a.q) a.logits[(size_t)t * a.E + e] = lg[0];
+  // this workgroup's share of the int8 token quantization: two blocks per wave
+  // pass, one per half-wave
   const int nblk = a.q * a.nb_h;
   const int b_end = min((int)(blockIdx.x + 1) * a.quant_per_wg, nblk);
-  // two blocks per pass, one per half-wave
-  for (int b0 = blockIdx.x * a.quant_per_wg; b0 < b_end; b0 += 2) {
+  for (int b0 = blockIdx.x * a.quant_per_wg + 2 * t; b0 < b_end; b0 += 2 * Q) {
     const int b = b0 + (lane >> 5), j = lane & 31;
     const bool ok = b < b_end;
     const float v = ok ? a.x[(size_t)b * 32 + j] : 0.0f;
@@ -120,8 +116,44 @@ struct PlanLds {
 // the expert of plan slot u (-1 if u is beyond the plan) and its column mask.
 // `write` (one workgroup) also computes the routing weights and stores the
 // routing (idx, gw) and the plan (size, ids, masks, weights per column).
+// Plan slot u from the per-token bitmaps in LDS (q > 1): the u-th set bit of
+// their union, its column mask, the union word of lane l (l < words) and the
+// plan size U. Uniform across the workgroup.
 template <int Q>
-__device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, int u, bool write, uint32_t& mask) {
+__device__ __forceinline__ int plan_slot(const DecodeArgs& a, const PlanLds& P, int u, uint32_t& mask,
+                                         uint32_t& uw, int& U) {
+  const int lane = threadIdx.x & 63;
+  const int nw = (a.E + 31) >> 5;
+  uw = 0;   // lane l < nw: word l of the union bitmap
+  if (lane < nw)
+#pragma unroll
+    for (int t = 0; t < Q; ++t)
+      if (t < a.q) uw |= P.bits[t][lane];
+  // slot u: uniform walk over the words
+  int e = -1, rem = u;
+  U = 0;
+  for (int w = 0; w < nw; ++w) {
+    const uint32_t word = (uint32_t)__builtin_amdgcn_readlane(uw, w);
+    const int c = __popc(word);
+    if (e < 0 && rem < c) {
+      uint32_t x = word;
+      for (int i = 0; i < rem; ++i) x &= x - 1;
+      e = 32 * w + (int)__builtin_ctz(x);
+    }
+    if (e < 0) rem -= c;
+    U += c;
+  }
+  mask = 0;
+  if (e >= 0)
+#pragma unroll
+    for (int t = 0; t < Q; ++t)
+      if (t < a.q && (P.bits[t][e >> 5] >> (e & 31) & 1u)) mask |= 1u << t;
+  return e;
+}
+
+template <int Q>
+__device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, int u, bool write, uint32_t& mask,
+                                             int* U_out = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   TopkPick p;
@@ -144,6 +176,7 @@ __device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, in
     }
     __syncthreads();
     mask = 1u;
+    if (U_out) *U_out = a.K;
     return P.e;
   } else {
     if (tid < 64) (&P.bits[0][0])[tid] = 0u;
@@ -163,29 +196,10 @@ __device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, in
     }
     __syncthreads();
     const int nw = (a.E + 31) >> 5;
-    uint32_t uw = 0;   // lane l < nw: word l of the union bitmap
-    if (lane < nw)
-#pragma unroll
-      for (int t = 0; t < Q; ++t)
-        if (t < a.q) uw |= P.bits[t][lane];
-    // slot u: uniform walk over the words
-    int e = -1, rem = u, U = 0;
-    for (int w = 0; w < nw; ++w) {
-      const uint32_t word = (uint32_t)__builtin_amdgcn_readlane(uw, w);
-      const int c = __popc(word);
-      if (e < 0 && rem < c) {
-        uint32_t x = word;
-        for (int i = 0; i < rem; ++i) x &= x - 1;
-        e = 32 * w + (int)__builtin_ctz(x);
-      }
-      if (e < 0) rem -= c;
-      U += c;
-    }
-    mask = 0;
-    if (e >= 0)
-#pragma unroll
-      for (int t = 0; t < Q; ++t)
-        if (t < a.q && (P.bits[t][e >> 5] >> (e & 31) & 1u)) mask |= 1u << t;
+    uint32_t uw;
+    int U;
+    const int e = plan_slot<Q>(a, P, u, mask, uw, U);
+    if (U_out) *U_out = U;
     if (write && wave == 0) {
       // lane s < U: the s-th distinct expert, its mask and weights
       int es = -1, rs = lane;
@@ -229,16 +243,12 @@ __device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, in
 // ------------------------------------------------------------ k_gateup
 // 8 waves; wave w owns rows 4w..4w+3 of both gate and up of the workgroup's 32
 // rows. Lanes cover NBL consecutive blocks each.
+// One item: rows rb*32 .. rb*32+31 of expert e's gate and up for plan slot u.
 template <int FMT, int Q>
-__global__ __launch_bounds__(512, (Q == 1) ? 2 : 1) void k_gateup(DecodeArgs a) {
+__device__ __forceinline__ void gateup_item(const DecodeArgs& a, int e, uint32_t mask, int u, int rb,
+                                            float (&s_a)[4][32]) {
   constexpr int NBL = (FMT == 4) ? 1 : 2;
   constexpr int RPW = 4;
-  __shared__ float s_a[4][32];
-  __shared__ PlanLds P;
-  const int u = blockIdx.y, rb = blockIdx.x;
-  uint32_t mask;
-  const int e = topk_and_plan<Q>(a, P, u, blockIdx.x == 0 && blockIdx.y == 0, mask);
-  if (e < 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row0 = rb * 32 + wave * RPW;
   const uint8_t* gbase = a.gate + (size_t)e * a.gu_stride;
@@ -305,6 +315,40 @@ __global__ __launch_bounds__(512, (Q == 1) ? 2 : 1) void k_gateup(DecodeArgs a) 
       if ((j & 3) == 0) reinterpret_cast<uint32_t*>(a.hq + slot * a.inter + (size_t)rb * 32)[j >> 2] = w;
       if (j == 0) a.dh[slot * a.nb_i + rb] = d;
     }
+  }
+}
+
+// One token: one workgroup per (plan slot, 32 rows), two workgroups per CU.
+template <int FMT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_gateup1(DecodeArgs a) {
+  __shared__ float s_a[4][32];
+  __shared__ PlanLds P;
+  uint32_t mask;
+  const int u = blockIdx.y;
+  const int e = topk_and_plan<1>(a, P, u, blockIdx.x == 0 && blockIdx.y == 0, mask);
+  if (e < 0) return;
+  gateup_item<FMT, 1>(a, e, mask, u, blockIdx.x, s_a);
+}
+
+// Two to four tokens: the kernel needs more registers, so one workgroup fits per
+// CU; a grid of one workgroup per CU selects once and walks the (slot, 32-row)
+// items with a stride, instead of paying the selection per item in several
+// passes of workgroups.
+template <int FMT, int Q>
+__global__ __launch_bounds__(512) void k_gateupq(DecodeArgs a) {
+  __shared__ float s_a[4][32];
+  __shared__ PlanLds P;
+  uint32_t mask;
+  int U;
+  topk_and_plan<Q>(a, P, 0, blockIdx.x == 0, mask, &U);
+  const int nrb = a.inter / 32;
+  for (int it = blockIdx.x; it < U * nrb; it += gridDim.x) {
+    const int u = it / nrb;
+    uint32_t uw;
+    int Uu;
+    const int e = plan_slot<Q>(a, P, u, mask, uw, Uu);
+    gateup_item<FMT, Q>(a, e, mask, u, it % nrb, s_a);
+    __syncthreads();   // s_a is reused by the next item
   }
 }
 
@@ -381,12 +425,15 @@ __global__ __launch_bounds__(256) void k_down(DecodeArgs a) {
 template <int FG, int FD, int Q>
 int launch_decode_t(const DecodeArgs& a, int U_max, hipStream_t s) {
   {
-    launch_kernel("route", k_route<Q>, dim3(a.E), dim3(64), s, a);
+    launch_kernel("route", k_route<Q>, dim3(a.E), dim3(64 * Q), s, a);
   }
   int st = launch_check("route");
   if (st) return st;
   {
-    launch_kernel("gateup", k_gateup<FG, Q>, dim3(a.inter / 32, U_max), dim3(512), s, a);
+    if constexpr (Q == 1)
+      launch_kernel("gateup", k_gateup1<FG>, dim3(a.inter / 32, U_max), dim3(512), s, a);
+    else
+      launch_kernel("gateup", k_gateupq<FG, Q>, dim3(device_cu_count()), dim3(512), s, a);
   }
   if ((st = launch_check("gateup"))) return st;
   const int rows_per_wg = 4 * (64 >> a.dn_lpr_log2);

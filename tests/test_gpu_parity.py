@@ -300,6 +300,21 @@ def test_decode_token_quant_bit_exact(q, rot):
     assert np.array_equal(dx.view(np.uint32), dx_ref.reshape(q, nb).view(np.uint32))
 
 
+@pytest.mark.parametrize("q", [1, 4])
+def test_decode_top8(q):
+    """Eight experts per token: eight selection rounds, and with one token the
+    down projection takes its planned experts in two groups."""
+    spec = gen.LayerSpec.tiny(n_experts=24, topk=8)
+    dl = qm.device.DeviceLayer(spec, seed=16)
+    x = gen.tokens(q, spec.hidden, seed=16)
+    out, ws = run_decode(dl, x)
+    ref, idx_ref, _ = moe.moe_tokens(oracle_layer(spec, 16, dl.w_router_host), x)
+    lay = qm.qmoe_workspace_layout(dl.desc, q)
+    idx = ws[lay["idx"]: lay["idx"] + 4 * q * 8].cpu().numpy().view(np.int32).reshape(q, 8)
+    assert np.array_equal(idx, idx_ref)
+    assert moe.rel_l2(out, ref) < TOL
+
+
 def test_decode_intermediate_activations():
     """The requantized SwiGLU output held in the workspace matches the oracle's
     int8 values except for rare one-code flips at rounding boundaries."""
