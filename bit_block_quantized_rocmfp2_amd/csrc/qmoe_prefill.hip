@@ -40,6 +40,7 @@ using namespace qmoe;
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kTileN = 64;   // pairs (tokens) per tile
 constexpr int kTileM = 64;   // weight rows per workgroup
@@ -299,6 +300,12 @@ struct StageLoader {
 // tile's pairs as up to four 16-column MFMA tiles (nn of them hold pairs). acc[m][n][r] accumulates row 16w + 4q + r,
 // column 16n + l % 16 (q = l / 16), in fp32: per block, the int32 MFMA result
 // times (weight scale x activation scale).
+// The scale products of one block form a 64-column x 16-row outer product per
+// matrix; one fp32 4-block MFMA (K = 1, one rounding per product, as a plain
+// fp32 multiply) leaves product (16n + l % 16, row 16w + 4q + r) in register
+// 4n + r of lane l, the same place as the int32 result it scales, which takes
+// the multiply off the vector ALU: per element and block only the convert and
+// the fused multiply-add remain.
 template <int FMT, int NMAT>
 __device__ __forceinline__ void stage_mma(const StageLds<FMT, NMAT>& S, const uint32_t cb[NMAT][4],
                                           float acc[NMAT][4][4], int nn) {
@@ -306,29 +313,27 @@ __device__ __forceinline__ void stage_mma(const StageLds<FMT, NMAT>& S, const ui
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i16 = lane & 15, q = lane >> 4;
   const int ra = 16 * wave + i16;          // A-operand row of this lane
-  const int rd = 16 * wave + 4 * q;        // first D row of this lane
 #pragma unroll 2
   for (int b = 0; b < kKB; ++b) {
     long A[NMAT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
       A[m] = expand_a<FMT>(&S.w[m][ra][b * LW], Fmt<FMT>::kHi ? S.h[m][Fmt<FMT>::kHi ? ra : 0][b] : 0u, q, cb[m]);
-    float4 sw[NMAT];
+    const float dl = S.dx[b][lane];        // activation scale of column `lane`
+    v16f p[NMAT];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) sw[m] = *reinterpret_cast<const float4*>(&S.s[m][b][rd]);
+    for (int m = 0; m < NMAT; ++m)
+      p[m] = __builtin_amdgcn_mfma_f32_16x16x1f32(S.s[m][b][ra], dl, v16f{}, 0, 0, 0);
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       if (n < nn) {   // 16-column subtiles beyond the tile's pairs are skipped (uniform)
       const int col = 16 * n + i16;
       const long B = *reinterpret_cast<const long*>(&S.x[col][b * 8 + 2 * q]);
-      const float d = S.dx[b][col];
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
         const v4i P = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[m], B, v4i{0, 0, 0, 0}, 0, 0, 0);
-        acc[m][n][0] = fmaf((float)P[0], sw[m].x * d, acc[m][n][0]);
-        acc[m][n][1] = fmaf((float)P[1], sw[m].y * d, acc[m][n][1]);
-        acc[m][n][2] = fmaf((float)P[2], sw[m].z * d, acc[m][n][2]);
-        acc[m][n][3] = fmaf((float)P[3], sw[m].w * d, acc[m][n][3]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[m][n][r] = fmaf((float)P[r], p[m][4 * n + r], acc[m][n][r]);
       }
       }
     }
