@@ -74,9 +74,11 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ W, 
 // power-of-two block count. The tree is evaluated depth first: its leaves are
 // visited in bit-reversed order and partial sums are kept per level like the
 // digits of a binary counter (level k holds a sum of 2^k leaves). Operands are
-// staged in LDS as fp64, 4 leaves at a time, converted once per workgroup.
+// staged in LDS as fp32, 4 leaves at a time (the fp16 weights widened exactly
+// once per workgroup), and widened to fp64 in registers at each use: exact, so
+// the products are those of an all-fp64 evaluation, at half the LDS bytes.
 constexpr int kRtE = 32, kRtT = 32, kRtLeaves = 4;
-constexpr int kRtStride = kRtLeaves * 32 + 2;   // doubles per LDS row (+2: spreads banks)
+constexpr int kRtStride = kRtLeaves * 32 + 4;   // floats per LDS row (+4: 16-byte reads of 16 rows hit distinct banks)
 constexpr int kRtLevels = 9;                    // up to 256 blocks (hidden <= 8192)
 
 __device__ __forceinline__ int bit_reverse(int v, int bits) {
@@ -86,8 +88,8 @@ __device__ __forceinline__ int bit_reverse(int v, int bits) {
 __global__ __launch_bounds__(256) void k_router_tiles(const uint16_t* __restrict__ W, const float* __restrict__ x,
                                                       int ntok, int E, int H, const double* __restrict__ bias,
                                                       double* __restrict__ logits) {
-  __shared__ double s_w[kRtE][kRtStride];
-  __shared__ double s_x[kRtT][kRtStride];
+  __shared__ float s_w[kRtE][kRtStride];
+  __shared__ float s_x[kRtT][kRtStride];
   const int tid = threadIdx.x;
   const int e_base = blockIdx.x * kRtE, t_base = blockIdx.y * kRtT;
   const int ei = tid >> 4, ti = tid & 15;   // experts ei, ei+16; tokens ti, ti+16
@@ -107,28 +109,29 @@ __global__ __launch_bounds__(256) void k_router_tiles(const uint16_t* __restrict
   for (int i0 = 0; i0 < P2; i0 += kRtLeaves) {
     {
       const int b = bit_reverse(i0 + lk, L);
-      double wv[16], xv[16];
+      float wv[16];
+      float4 xv[4];
       if (b < nb) {
         const u32x4* wp = reinterpret_cast<const u32x4*>(W + (size_t)le * H + (size_t)b * 32 + 16 * lh);
         const u32x4 u0 = wp[0], u1 = wp[1];
         const uint32_t hw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-        for (int j = 0; j < 16; ++j) wv[j] = (double)half_bits_to_float((hw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+        for (int j = 0; j < 16; ++j) wv[j] = half_bits_to_float((hw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
         const float4* xp = reinterpret_cast<const float4*>(x + (size_t)lt * H + (size_t)b * 32 + 16 * lh);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 f = xp[j];
-          xv[4 * j] = f.x; xv[4 * j + 1] = f.y; xv[4 * j + 2] = f.z; xv[4 * j + 3] = f.w;
-        }
+        for (int j = 0; j < 4; ++j) xv[j] = xp[j];
       } else {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) wv[j] = xv[j] = 0.0;
+        for (int j = 0; j < 16; ++j) wv[j] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xv[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       }
       __syncthreads();   // the previous chunk's reads are done
 #pragma unroll
-      for (int j = 0; j < 16; j += 2) {
-        *reinterpret_cast<double2*>(&s_w[lr][lk * 32 + 16 * lh + j]) = make_double2(wv[j], wv[j + 1]);
-        *reinterpret_cast<double2*>(&s_x[lr][lk * 32 + 16 * lh + j]) = make_double2(xv[j], xv[j + 1]);
+      for (int j = 0; j < 4; ++j) {
+        *reinterpret_cast<float4*>(&s_w[lr][lk * 32 + 16 * lh + 4 * j]) =
+            make_float4(wv[4 * j], wv[4 * j + 1], wv[4 * j + 2], wv[4 * j + 3]);
+        *reinterpret_cast<float4*>(&s_x[lr][lk * 32 + 16 * lh + 4 * j]) = xv[j];
       }
       __syncthreads();
     }
@@ -138,16 +141,22 @@ __global__ __launch_bounds__(256) void k_router_tiles(const uint16_t* __restrict
       double acc[4] = {0.0, 0.0, 0.0, 0.0};
       const bool real = bit_reverse(i, L) < nb;   // padding leaves are +0
       if (real) {
-#pragma unroll 4
-        for (int j = 0; j < 32; j += 2) {
-          const double2 w0 = *reinterpret_cast<const double2*>(&s_w[ei][k * 32 + j]);
-          const double2 w1 = *reinterpret_cast<const double2*>(&s_w[ei + 16][k * 32 + j]);
-          const double2 x0 = *reinterpret_cast<const double2*>(&s_x[ti][k * 32 + j]);
-          const double2 x1 = *reinterpret_cast<const double2*>(&s_x[ti + 16][k * 32 + j]);
-          acc[0] = fma(w0.x, x0.x, acc[0]); acc[0] = fma(w0.y, x0.y, acc[0]);
-          acc[1] = fma(w0.x, x1.x, acc[1]); acc[1] = fma(w0.y, x1.y, acc[1]);
-          acc[2] = fma(w1.x, x0.x, acc[2]); acc[2] = fma(w1.y, x0.y, acc[2]);
-          acc[3] = fma(w1.x, x1.x, acc[3]); acc[3] = fma(w1.y, x1.y, acc[3]);
+#pragma unroll 2
+        for (int j = 0; j < 32; j += 4) {
+          const float4 w0 = *reinterpret_cast<const float4*>(&s_w[ei][k * 32 + j]);
+          const float4 w1 = *reinterpret_cast<const float4*>(&s_w[ei + 16][k * 32 + j]);
+          const float4 x0 = *reinterpret_cast<const float4*>(&s_x[ti][k * 32 + j]);
+          const float4 x1 = *reinterpret_cast<const float4*>(&s_x[ti + 16][k * 32 + j]);
+          const float fw0[4] = {w0.x, w0.y, w0.z, w0.w}, fw1[4] = {w1.x, w1.y, w1.z, w1.w};
+          const float fx0[4] = {x0.x, x0.y, x0.z, x0.w}, fx1[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const double a0 = fw0[u], a1 = fw1[u], b0 = fx0[u], b1 = fx1[u];
+            acc[0] = fma(a0, b0, acc[0]);
+            acc[1] = fma(a0, b1, acc[1]);
+            acc[2] = fma(a1, b0, acc[2]);
+            acc[3] = fma(a1, b1, acc[3]);
+          }
         }
       }
       // push the leaf: carry through the occupied levels (bits of i), left + right
