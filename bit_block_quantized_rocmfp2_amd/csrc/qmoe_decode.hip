@@ -265,16 +265,21 @@ __device__ __forceinline__ void gateup_item(const DecodeArgs& a, int e, uint32_t
   for (int c0 = 0; c0 < nb; c0 += 64 * NBL) {
     const int b = c0 + lane * NBL;
     if (b < nb) {
+      // the activations (cache-resident) are requested first, so the rows can be
+      // used in load order while later rows are still in flight
+      Acts<NBL> act[Q];
+#pragma unroll
+      for (int t = 0; t < Q; ++t)
+        if (mask >> t & 1) act[t].load(a.xq + (size_t)t * nb * 32, a.dx + (size_t)t * nb, b);
       Blocks<FMT, NBL> bg[RPW], bu[RPW];
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         bg[r].load(gbase + (size_t)(row0 + r) * a.gu_row_bytes, nb, b);
         bu[r].load(ubase + (size_t)(row0 + r) * a.gu_row_bytes, nb, b);
       }
-      Acts<NBL> act[Q];
-#pragma unroll
-      for (int t = 0; t < Q; ++t)
-        if (mask >> t & 1) act[t].load(a.xq + (size_t)t * nb * 32, a.dx + (size_t)t * nb, b);
+      // keep every load above this point: one memory round trip per wave (left
+      // to itself the scheduler sinks the scale loads below the first products)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < RPW; ++r)
 #pragma unroll
