@@ -427,6 +427,92 @@ __global__ __launch_bounds__(256) void k_down(DecodeArgs a) {
   }
 }
 
+// One token, at most six planned experts, one pass over the blocks and at most
+// 16 KB of activations (the common shape; the host sends other shapes to
+// k_down). The workgroup copies the activations of the planned experts to LDS
+// with one 16-byte load per thread and piece (every lane of k_down loads its own
+// copy, 8x the bytes through the vector cache per CU), and requests all weight
+// blocks of the lane behind them, before any is used. The accumulation order is
+// that of k_down.
+constexpr int kDown1MaxU = 6;
+constexpr int kDown1ActBytes = 16384;
+template <int FMT>
+__global__ __launch_bounds__(256) void k_down1(DecodeArgs a) {
+  constexpr int NBL = (FMT == 4) ? 1 : 2;
+  constexpr int UB = kDown1MaxU;
+  const int lpr_log2 = a.dn_lpr_log2;
+  const int lpr = 1 << lpr_log2;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int sub = lane >> lpr_log2, sl = lane & (lpr - 1);
+  const int row = (blockIdx.x * 4 + wave) * (64 >> lpr_log2) + sub;
+  __shared__ int s_plan[kPlanWOff + 4 * kPlanMax];
+  __shared__ u32x4 s_hq[kDown1ActBytes / 16];
+  __shared__ u32x4 s_dh[256];   // >= kDown1ActBytes / 32 / 4, one piece per thread
+  s_plan[tid] = a.plan[tid];
+  __syncthreads();
+  const int U = s_plan[0];
+  const float* pw = reinterpret_cast<const float*>(s_plan + kPlanWOff);
+  const int nb = a.nb_i;
+  // activations of slots (u, token 0) = 4u: U rows of inter bytes and nb scales
+  const int nq = U * a.inter / 16, nd = U * nb / 4;
+  // every thread issues every load (indices clamped into range; only the LDS
+  // stores below are restricted), so no loaded value is defined conditionally
+  u32x4 hv[4], dv;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = min(tid + 256 * k, nq - 1);
+    const int u = (16 * i) / a.inter, off = (16 * i) % a.inter;
+    hv[k] = *reinterpret_cast<const u32x4*>(a.hq + (size_t)u * 4 * a.inter + off);
+  }
+  {
+    const int i = min(tid, nd - 1);
+    const int u = (4 * i) / nb, off = (4 * i) % nb;
+    dv = *reinterpret_cast<const u32x4*>(a.dh + (size_t)u * 4 * nb + off);
+  }
+  const int b = sl * NBL;
+  const bool ok = row < a.hidden && b < nb;
+  // weight loads are unconditional too (row and block clamped, idle slots read
+  // expert 0): a load inside a branch makes the wait before the LDS stores
+  // below count as if it had not been issued
+  const int rowc = min(row, a.hidden - 1), bc = min(b, nb - NBL);
+  int ej[UB];
+  uint32_t cb[UB][4];
+  Blocks<FMT, NBL> bl[UB];
+#pragma unroll
+  for (int j = 0; j < UB; ++j) {
+    ej[j] = (j < U) ? s_plan[kPlanIdOff + j] : 0;
+    load_codebook<FMT>(a.cb_down + ((size_t)ej[j] << FMT), cb[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < UB; ++j)
+    bl[j].load(a.down + (size_t)ej[j] * a.dn_stride + (size_t)rowc * a.dn_row_bytes, nb, bc);
+  __builtin_amdgcn_sched_barrier(0);
+  // pieces beyond nq / nd land in LDS slots that are never read
+#pragma unroll
+  for (int k = 0; k < 4; ++k) s_hq[tid + 256 * k] = hv[k];
+  s_dh[tid] = dv;
+  __syncthreads();
+  const int8_t* hq = reinterpret_cast<const int8_t*>(s_hq);
+  const float* dh = reinterpret_cast<const float*>(s_dh);
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < UB; ++j)
+    if (ok && j < U) {
+      const float wgt = pw[4 * j];
+      Acts<NBL> act;
+      act.load(hq + (size_t)j * a.inter, dh + (size_t)j * nb, b);
+#pragma unroll
+      for (int i = 0; i < NBL; ++i) {
+        uint32_t w[8];
+        bl[j].expand(i, cb[j], w);
+        const int p = block_dot(w, act.q[i]);
+        acc = fmaf((float)p, bl[j].scale(i) * act.d[i] * wgt, acc);
+      }
+    }
+  const float v = group_sum(acc, lpr);
+  if (sl == 0 && row < a.hidden) a.out[row] = v;
+}
+
 template <int FG, int FD, int Q>
 int launch_decode_t(const DecodeArgs& a, int U_max, hipStream_t s) {
   {
@@ -443,7 +529,13 @@ int launch_decode_t(const DecodeArgs& a, int U_max, hipStream_t s) {
   if ((st = launch_check("gateup"))) return st;
   const int rows_per_wg = 4 * (64 >> a.dn_lpr_log2);
   {
-    launch_kernel("down", k_down<FD, Q>, dim3((a.hidden + rows_per_wg - 1) / rows_per_wg), dim3(256), s, a);
+    const dim3 grid((a.hidden + rows_per_wg - 1) / rows_per_wg);
+    constexpr int NBL = (FD == 4) ? 1 : 2;
+    if (Q == 1 && U_max <= kDown1MaxU && a.nb_i <= (NBL << a.dn_lpr_log2) && a.nb_i % 4 == 0 &&
+        U_max * a.inter <= kDown1ActBytes)
+      launch_kernel("down", k_down1<FD>, grid, dim3(256), s, a);
+    else
+      launch_kernel("down", k_down<FD, Q>, grid, dim3(256), s, a);
   }
   return launch_check("down");
 }
