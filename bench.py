@@ -31,10 +31,10 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, published (TOPS)
-# HBM bytes per launch of k_gateup<2,1> (decode q=1), from rocprofv3 FETCH_SIZE and WRITE_SIZE runs scaled by
+# HBM bytes per launch of k_gateup1<2> (decode q=1), from rocprofv3 FETCH_SIZE and WRITE_SIZE runs scaled by
 # a 256 MiB device copy (profiles/hbm_traffic_decode_q1_prefill_8k.md). Must be re-measured (or set to None)
 # whenever that kernel changes.
-GATEUP_Q1_TRAFFIC_BYTES = 31841799
+GATEUP_Q1_TRAFFIC_BYTES = 31851117
 
 WORKLOAD = ("MoE decode layer q=1: hidden 4096, 256 routed experts, expert intermediate 2048, router W fp16 "
             "N(0,0.02) with softmax top-6, gate/up ROCmFP2 (4-entry per-expert codebooks), down ROCmFP3 "
@@ -152,7 +152,7 @@ def main():
     achieved = spec.topk * gateup_bytes / (gu_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": GATEUP_Q1_TRAFFIC_BYTES,
-                "kernel": "k_gateup<2,1> (6 experts x gate+up FP2 = 31,457,280 algorithmic bytes per launch)"}
+                "kernel": "k_gateup1<2> (6 experts x gate+up FP2 = 31,457,280 algorithmic bytes per launch)"}
     down_gbs = spec.topk * down_bytes / (kern["down"] * 1e-3) / 1e9
 
     extra = {"decode_q1": {"us_per_call": round(ms * 1e3, 2), "tokens_per_s": round(1.0 / (ms * 1e-3), 1),
