@@ -427,6 +427,140 @@ __global__ __launch_bounds__(256) void k_down(DecodeArgs a) {
   }
 }
 
+// Two to four tokens, when one pass covers the blocks and the routed
+// (expert, token) slots' activations fit 48 KB: the workgroup lists the slots of
+// the plan, copies their activations to LDS with direct 16-byte global -> LDS
+// loads (no registers), and requests the weight blocks of up to 12 experts in
+// the same round trip; each block is expanded once and applied to every routed
+// column. k_down instead loads each lane's own copy of every slot's activations
+// after that expert's weights. The per-lane accumulation order is that of k_down
+// (experts ascending, then columns, then the lane's blocks).
+constexpr int kDownqActPieces = 48 * 1024 / 16;   // 16-byte pieces of staged activations
+constexpr int kDownqMaxSlots = 32;
+template <int FMT, int Q>
+__global__ __launch_bounds__(256) void k_downq(DecodeArgs a) {
+  constexpr int NBL = (FMT == 4) ? 1 : 2;
+  constexpr int UB = 12;
+  constexpr int CPL = 2 * NBL;   // 16-byte activation pieces per lane and slot
+  typedef __attribute__((address_space(3))) void lds_void;
+  const int lpr_log2 = a.dn_lpr_log2;
+  const int lpr = 1 << lpr_log2;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int sub = lane >> lpr_log2, sl = lane & (lpr - 1);
+  const int row = (blockIdx.x * 4 + wave) * (64 >> lpr_log2) + sub;
+  __shared__ int s_plan[kPlanWOff + 4 * kPlanMax];
+  __shared__ int s_slot[kDownqMaxSlots];      // compact slot c -> u * 4 + t
+  __shared__ int s_cidx[4 * kPlanMax];        // u * 4 + t -> compact slot
+  __shared__ int s_nslot;
+  __shared__ u32x4 s_act[kDownqActPieces + 256];
+  __shared__ u32x4 s_dh[kDownqMaxSlots * 16 + 256];
+  s_plan[tid] = a.plan[tid];
+  __syncthreads();
+  const int U = s_plan[0];
+  const float* pw = reinterpret_cast<const float*>(s_plan + kPlanWOff);
+  const int nb = a.nb_i;
+  if (wave == 0) {
+    // lane u < U: its routed columns; exclusive prefix of the counts by ballots
+    const uint32_t m = (lane < U) ? ((uint32_t)s_plan[kPlanMaskOff + lane] & ((1u << Q) - 1u)) : 0u;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int base = 0, total = 0;
+#pragma unroll
+    for (int t = 0; t < Q; ++t) {
+      const uint64_t bt = __ballot((m >> t) & 1u);
+      base += __popcll(bt & lt);
+      total += __popcll(bt);
+    }
+    int c = base;
+#pragma unroll
+    for (int t = 0; t < Q; ++t)
+      if ((m >> t) & 1u) {
+        s_slot[c] = lane * 4 + t;
+        s_cidx[lane * 4 + t] = c;
+        ++c;
+      }
+    if (lane == 0) s_nslot = total;
+  }
+  __syncthreads();
+  const int nslot = s_nslot;
+  const int b = sl * NBL;
+  const bool ok = row < a.hidden && b < nb;
+  const int rowc = min(row, a.hidden - 1), bc = min(b, nb - NBL);
+  // weights of the first group of experts (unconditional, clamped loads)
+  int ej[UB];
+  uint32_t cb[UB][4];
+  Blocks<FMT, NBL> bl[UB];
+#pragma unroll
+  for (int j = 0; j < UB; ++j) {
+    ej[j] = (j < U) ? s_plan[kPlanIdOff + j] : 0;
+    load_codebook<FMT>(a.cb_down + ((size_t)ej[j] << FMT), cb[j]);
+    bl[j].load(a.down + (size_t)ej[j] * a.dn_stride + (size_t)rowc * a.dn_row_bytes, nb, bc);
+  }
+  // activations of the listed slots: LDS piece (within slot c) m * lpr + l holds
+  // piece l * CPL + m of the slot's row, so that each read of the lanes of one
+  // row touches consecutive pieces; pieces past the end repeat the last slot
+  const int pps = nb * 2;   // pieces per slot (= lpr * CPL)
+  const int nq = nslot * pps;
+  for (int r0 = 0; r0 < nq; r0 += 256) {
+    const int P = r0 + 64 * wave + lane;
+    const int c = min(P / pps, nslot - 1), within = P % pps;
+    const int g = (within % lpr) * CPL + within / lpr;
+    const int8_t* src = a.hq + (size_t)s_slot[c] * a.inter + (size_t)g * 16;
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(s_act + r0 + 64 * wave), 16, 0, 0);
+  }
+  const int nd = nslot * (nb / 4);   // 16-byte pieces of scales (4 per piece)
+  for (int r0 = 0; r0 < nd; r0 += 256) {
+    const int P = r0 + 64 * wave + lane;
+    const int c = min(P / (nb / 4), nslot - 1), within = P % (nb / 4);
+    const float* src = a.dh + (size_t)s_slot[c] * nb + (size_t)within * 4;
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(s_dh + r0 + 64 * wave), 16, 0, 0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const float* dh = reinterpret_cast<const float*>(s_dh);
+  float acc[Q];
+#pragma unroll
+  for (int t = 0; t < Q; ++t) acc[t] = 0.0f;
+  for (int u0 = 0; u0 < U; u0 += UB) {
+    if (u0 > 0) {   // further groups (more than UB planned experts)
+#pragma unroll
+      for (int j = 0; j < UB; ++j) {
+        ej[j] = (u0 + j < U) ? s_plan[kPlanIdOff + u0 + j] : 0;
+        load_codebook<FMT>(a.cb_down + ((size_t)ej[j] << FMT), cb[j]);
+        bl[j].load(a.down + (size_t)ej[j] * a.dn_stride + (size_t)rowc * a.dn_row_bytes, nb, bc);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < UB; ++j) {
+      const int u = u0 + j;
+      if (ok && u < U) {
+        const uint32_t mask = (uint32_t)s_plan[kPlanMaskOff + u];
+        uint32_t w[NBL][8];
+#pragma unroll
+        for (int i = 0; i < NBL; ++i) bl[j].expand(i, cb[j], w[i]);
+#pragma unroll
+        for (int t = 0; t < Q; ++t)
+          if (mask >> t & 1) {
+            const float wgt = pw[4 * u + t];
+            const int c = s_cidx[u * 4 + t];
+#pragma unroll
+            for (int i = 0; i < NBL; ++i) {
+              const u32x4 x0 = s_act[c * pps + (2 * i) * lpr + sl];
+              const u32x4 x1 = s_act[c * pps + (2 * i + 1) * lpr + sl];
+              const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+              const int p = block_dot(w[i], xw);
+              acc[t] = fmaf((float)p, bl[j].scale(i) * dh[c * nb + b + i] * wgt, acc[t]);
+            }
+          }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < Q; ++t) {
+    const float v = group_sum(acc[t], lpr);
+    if (sl == 0 && row < a.hidden) a.out[(size_t)t * a.hidden + row] = v;
+  }
+}
+
 // One token, at most six planned experts, one pass over the blocks and at most
 // 16 KB of activations (the common shape; the host sends other shapes to
 // k_down). The workgroup copies the activations of the planned experts to LDS
@@ -534,6 +668,9 @@ int launch_decode_t(const DecodeArgs& a, int U_max, hipStream_t s) {
     if (Q == 1 && U_max <= kDown1MaxU && a.nb_i <= (NBL << a.dn_lpr_log2) && a.nb_i % 4 == 0 &&
         U_max * a.inter <= kDown1ActBytes)
       launch_kernel("down", k_down1<FD>, grid, dim3(256), s, a);
+    else if (Q > 1 && a.nb_i == (NBL << a.dn_lpr_log2) && a.nb_i % 4 == 0 && Q * a.K <= kDownqMaxSlots &&
+             Q * a.K * a.inter <= kDownqActPieces * 16)
+      launch_kernel("down", k_downq<FD, Q>, grid, dim3(256), s, a);
     else
       launch_kernel("down", k_down<FD, Q>, grid, dim3(256), s, a);
   }
