@@ -315,6 +315,25 @@ def test_decode_top8(q):
     assert moe.rel_l2(out, ref) < TOL
 
 
+@pytest.mark.parametrize("q,inter,topk", [(1, 768, 6), (3, 768, 6), (1, 2048, 6), (2, 2048, 6), (4, 2048, 6),
+                                           (4, 2048, 8)])
+def test_decode_down_variants(q, inter, topk):
+    """The down projection runs one of three kernels by shape: one token with at
+    most six experts and one pass over the blocks; several tokens whose routed
+    activations fit the workgroup's LDS copy (up to 48 KB); and the general
+    kernel (inter 768 needs two passes of the lanes; four tokens x top-8 x 2 KB
+    exceed the copy). Each matches the oracle."""
+    spec = gen.LayerSpec(hidden=512, inter=inter, n_experts=16, topk=topk)
+    dl = qm.device.DeviceLayer(spec, seed=17)
+    x = gen.tokens(q, spec.hidden, seed=170 + q)
+    out, ws = run_decode(dl, x)
+    ref, idx_ref, _ = moe.moe_tokens(oracle_layer(spec, 17, dl.w_router_host), x)
+    lay = qm.qmoe_workspace_layout(dl.desc, q)
+    idx = ws[lay["idx"]: lay["idx"] + 4 * q * topk].cpu().numpy().view(np.int32).reshape(q, topk)
+    assert np.array_equal(idx, idx_ref)
+    assert moe.rel_l2(out, ref) < TOL
+
+
 def test_decode_intermediate_activations():
     """The requantized SwiGLU output held in the workspace matches the oracle's
     int8 values except for rare one-code flips at rounding boundaries."""
