@@ -203,10 +203,21 @@ def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
     ms = t.ms / K
     mean_bytes = float(np.mean([U[i % len(groups)] for i in range(K)])) * per_expert
     gbs = mean_bytes / (ms * 1e-3) / 1e9
+    qm.qmoe_timing_enable(True)
+    for i in range(K):
+        qm.qmoe_decode_layer(dl.desc, groups[i % len(groups)], out, ws)
+    torch.cuda.synchronize()
+    kern = {}
+    for name in ("route", "gateup", "down"):
+        avg, _ = kernel_avg_ms(qm, name)
+        if avg:
+            kern[name] = round(avg * 1e3, 2)
+    qm.qmoe_timing_enable(False)
     res["decode_q4"] = {"us_per_call": round(ms * 1e3, 2), "tokens_per_s": round(4 / (ms * 1e-3), 1),
                         "mean_distinct_experts": round(float(np.mean(U)), 2), "effective_GBps": round(gbs, 1),
-                        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "groups": len(groups)}
-    log(f"decode q=4: {ms * 1e3:.2f} us/call, U={np.mean(U):.2f}, {gbs:.1f} GB/s")
+                        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "groups": len(groups), "kernel_us": kern}
+    log(f"decode q=4: {ms * 1e3:.2f} us/call, U={np.mean(U):.2f}, {gbs:.1f} GB/s; kernels (us): "
+        + ", ".join(f"{k}={v}" for k, v in kern.items()))
 
     # ---------------------------------------------------------------- prefill 8K (Zipf)
     try:

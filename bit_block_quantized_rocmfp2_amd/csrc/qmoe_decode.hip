@@ -244,6 +244,38 @@ __device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, in
 // 8 waves; wave w owns rows 4w..4w+3 of both gate and up of the workgroup's 32
 // rows. Lanes cover NBL consecutive blocks each.
 // One item: rows rb*32 .. rb*32+31 of expert e's gate and up for plan slot u.
+// SwiGLU of the workgroup's 32 rows (wave w holds rows RPW*w .. RPW*w + RPW-1 as
+// per-lane partial sums) and requantization of the 32-row block (+ H32) for each
+// routed column of slot u.
+template <int Q, int RPW>
+__device__ __forceinline__ void gateup_epilogue(const DecodeArgs& a, uint32_t mask, int u, int rb,
+                                                const float (&ag)[RPW][Q], const float (&au)[RPW][Q],
+                                                float (&s_a)[4][32]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int t = 0; t < Q; ++t)
+      if (mask >> t & 1) {
+        const float gv = group_sum(ag[r][t], 64);
+        const float uv = group_sum(au[r][t], 64);
+        if (lane == 0) s_a[t][wave * RPW + r] = gv / (1.0f + expf(-gv)) * uv;
+      }
+  __syncthreads();
+  // requantize the 32-row block: half-wave h of wave w takes column 2w + h
+  if (wave < (Q + 1) / 2) {
+    const int t = 2 * wave + (lane >> 5), j = lane & 31;
+    const bool act = t < Q && (mask >> t & 1);
+    float d;
+    const uint32_t w = quant_block32_lanes(act ? s_a[t][j] : 0.0f, a.rot_down, &d);
+    if (act) {
+      const size_t slot = (size_t)u * 4 + t;
+      if ((j & 3) == 0) reinterpret_cast<uint32_t*>(a.hq + slot * a.inter + (size_t)rb * 32)[j >> 2] = w;
+      if (j == 0) a.dh[slot * a.nb_i + rb] = d;
+    }
+  }
+}
+
 template <int FMT, int Q>
 __device__ __forceinline__ void gateup_item(const DecodeArgs& a, int e, uint32_t mask, int u, int rb,
                                             float (&s_a)[4][32]) {
@@ -299,28 +331,7 @@ __device__ __forceinline__ void gateup_item(const DecodeArgs& a, int e, uint32_t
         }
     }
   }
-#pragma unroll
-  for (int r = 0; r < RPW; ++r)
-#pragma unroll
-    for (int t = 0; t < Q; ++t)
-      if (mask >> t & 1) {
-        const float gv = group_sum(ag[r][t], 64);
-        const float uv = group_sum(au[r][t], 64);
-        if (lane == 0) s_a[t][wave * RPW + r] = gv / (1.0f + expf(-gv)) * uv;
-      }
-  __syncthreads();
-  // requantize the 32-row block: half-wave h of wave w takes column 2w + h
-  if (wave < (Q + 1) / 2) {
-    const int t = 2 * wave + (lane >> 5), j = lane & 31;
-    const bool act = t < Q && (mask >> t & 1);
-    float d;
-    const uint32_t w = quant_block32_lanes(act ? s_a[t][j] : 0.0f, a.rot_down, &d);
-    if (act) {
-      const size_t slot = (size_t)u * 4 + t;
-      if ((j & 3) == 0) reinterpret_cast<uint32_t*>(a.hq + slot * a.inter + (size_t)rb * 32)[j >> 2] = w;
-      if (j == 0) a.dh[slot * a.nb_i + rb] = d;
-    }
-  }
+  gateup_epilogue<Q, RPW>(a, mask, u, rb, ag, au, s_a);
 }
 
 // One token: one workgroup per (plan slot, 32 rows), two workgroups per CU.
@@ -353,6 +364,97 @@ __global__ __launch_bounds__(512) void k_gateupq(DecodeArgs a) {
     int Uu;
     const int e = plan_slot<Q>(a, P, u, mask, uw, Uu);
     gateup_item<FMT, Q>(a, e, mask, u, it % nrb, s_a);
+    __syncthreads();   // s_a is reused by the next item
+  }
+}
+
+// Two to four tokens and one pass over the blocks: 1024-thread workgroups (16
+// waves of two gate and two up rows each) walk the same items with the tokens'
+// int8 blocks and scales copied to LDS once. That leaves ~90 registers per lane,
+// so four waves per SIMD issue the vector instructions (k_gateupq, at 223
+// registers, runs two). The LDS copy puts piece g (16 bytes) of a token row at
+// (g % CPL) * 64 + g / CPL and the scale of block k at (k % NBL) * 64 + k / NBL,
+// so that the 64 lanes of a read touch consecutive addresses. The per-lane
+// accumulation order is that of gateup_item.
+template <int FMT, int Q>
+__global__ __launch_bounds__(1024) void k_gateupq2(DecodeArgs a) {
+  constexpr int NBL = (FMT == 4) ? 1 : 2;
+  constexpr int RPW = 2;
+  constexpr int CPL = 2 * NBL;
+  __shared__ float s_a[4][32];
+  __shared__ PlanLds P;
+  __shared__ u32x4 s_xq[Q * 256];   // per token: 64 lanes x CPL pieces
+  __shared__ float s_dx[Q * 128];   // per token: 64 lanes x NBL scales
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  uint32_t mask0;
+  int U;
+  topk_and_plan<Q>(a, P, 0, blockIdx.x == 0, mask0, &U);
+  const int nb = a.nb_h;
+  for (int i = tid; i < Q * nb * 2; i += 1024) {
+    const int t = i / (nb * 2), g = i % (nb * 2);
+    s_xq[t * 256 + (g % CPL) * 64 + g / CPL] = reinterpret_cast<const u32x4*>(a.xq)[i];
+  }
+  for (int i = tid; i < Q * nb; i += 1024) {
+    const int t = i / nb, k = i % nb;
+    s_dx[t * 128 + (k % NBL) * 64 + k / NBL] = a.dx[i];
+  }
+  __syncthreads();
+  const int nrb = a.inter / 32;
+  const int b = lane * NBL;
+  const bool ok = b < nb;
+  const int bc = min(b, nb - NBL);
+  for (int it = blockIdx.x; it < U * nrb; it += gridDim.x) {
+    const int u = it / nrb, rb = it % nrb;
+    uint32_t mask, uw;
+    int Uu;
+    const int e = plan_slot<Q>(a, P, u, mask, uw, Uu);
+    const int row0 = rb * 32 + wave * RPW;
+    const uint8_t* gbase = a.gate + (size_t)e * a.gu_stride;
+    const uint8_t* ubase = a.up + (size_t)e * a.gu_stride;
+    uint32_t cbg[4], cbu[4];
+    load_codebook<FMT>(a.cb_gate + ((size_t)e << FMT), cbg);
+    load_codebook<FMT>(a.cb_up + ((size_t)e << FMT), cbu);
+    Blocks<FMT, NBL> bg[RPW], bu[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      bg[r].load(gbase + (size_t)(row0 + r) * a.gu_row_bytes, nb, bc);
+      bu[r].load(ubase + (size_t)(row0 + r) * a.gu_row_bytes, nb, bc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float ag[RPW][Q], au[RPW][Q];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int t = 0; t < Q; ++t) ag[r][t] = au[r][t] = 0.0f;
+    if (ok) {
+#pragma unroll
+      for (int i = 0; i < NBL; ++i) {
+        uint32_t wg[RPW][8], wu[RPW][8];
+        float sg[RPW], su[RPW];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          bg[r].expand(i, cbg, wg[r]);
+          bu[r].expand(i, cbu, wu[r]);
+          sg[r] = bg[r].scale(i);
+          su[r] = bu[r].scale(i);
+        }
+#pragma unroll
+        for (int t = 0; t < Q; ++t)
+          if (mask >> t & 1) {
+            const u32x4 x0 = s_xq[t * 256 + (2 * i) * 64 + lane], x1 = s_xq[t * 256 + (2 * i + 1) * 64 + lane];
+            const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            const float dxt = s_dx[t * 128 + i * 64 + lane];
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+              const int pg = block_dot(wg[r], xw);
+              const int pu = block_dot(wu[r], xw);
+              ag[r][t] = fmaf((float)pg, sg[r] * dxt, ag[r][t]);
+              au[r][t] = fmaf((float)pu, su[r] * dxt, au[r][t]);
+            }
+          }
+      }
+    }
+    gateup_epilogue<Q, RPW>(a, mask, u, rb, ag, au, s_a);
     __syncthreads();   // s_a is reused by the next item
   }
 }
@@ -658,7 +760,10 @@ int launch_decode_t(const DecodeArgs& a, int U_max, hipStream_t s) {
     if constexpr (Q == 1)
       launch_kernel("gateup", k_gateup1<FG>, dim3(a.inter / 32, U_max), dim3(512), s, a);
     else
-      launch_kernel("gateup", k_gateupq<FG, Q>, dim3(device_cu_count()), dim3(512), s, a);
+      if (a.nb_h <= 64 * ((FG == 4) ? 1 : 2))
+        launch_kernel("gateup", k_gateupq2<FG, Q>, dim3(device_cu_count()), dim3(1024), s, a);
+      else
+        launch_kernel("gateup", k_gateupq<FG, Q>, dim3(device_cu_count()), dim3(512), s, a);
   }
   if ((st = launch_check("gateup"))) return st;
   const int rows_per_wg = 4 * (64 >> a.dn_lpr_log2);
