@@ -17,20 +17,25 @@
 //
 //   k_route    one workgroup per expert, one wave per token: fp64 logits; the
 //              workgroups also share the int8 quantization of the tokens.
-//   k_gateup   one workgroup per (planned expert slot, 32 rows). Every
-//              workgroup first selects the top-k of each token from the logits
-//              and builds the plan itself (the union of the chosen experts in
-//              ascending id, a column mask and the routing weights per expert),
-//              so no workgroup waits for another; workgroup (0, 0) also writes
-//              the routing and the plan out. Then the gate and up rows are
-//              streamed once (all loads of a wave issued before the first use),
-//              each block expanded once for every column routed to the expert;
-//              SwiGLU, then requantization of the 32-row block (+ H32) for the
-//              down projection. Slots beyond the plan's size exit.
+//   k_gateup   the gate/up launch. Every workgroup first selects the top-k of
+//              each token from the logits and builds the plan itself (the union
+//              of the chosen experts in ascending id, a column mask and the
+//              routing weights per expert), so no workgroup waits for another;
+//              the first workgroup also writes the routing and the plan out.
+//              Then the gate and up rows of its items (32 rows of one planned
+//              expert) are streamed once, all loads of a wave issued before the
+//              first use, each block expanded once for every column routed to
+//              the expert; SwiGLU, then requantization of the 32-row block
+//              (+ H32) for the down projection. One token: k_gateup1, one
+//              workgroup per item. Several tokens: one workgroup per CU walks
+//              the items (k_gateupq2 with the tokens' blocks in LDS when a row
+//              fits one pass of the lanes, k_gateupq otherwise).
 //   k_down     one workgroup per group of rows: the plan is read in one round
 //              trip, the rows of every planned expert are loaded together, per
 //              column contributions are accumulated per lane in ascending
-//              expert id with the routing weights, and reduced once.
+//              expert id with the routing weights, and reduced once. k_down1
+//              (one token) and k_downq (several) copy the routed activations
+//              to LDS once per workgroup; k_down serves the other shapes.
 // Kernel boundaries make each launch's results visible to the next across the
 // 8 XCDs (separate L2 caches); no workgroup waits for another inside a launch.
 #include <hip/hip_runtime.h>
