@@ -222,6 +222,19 @@ def test_route_hidden_8192(ntok):
         assert moe.rel_l2(out, ref) < TOL
 
 
+@pytest.mark.parametrize("q", [2, 4])
+def test_decode_hidden_8192(q):
+    """The largest hidden size through the whole decode layer with several
+    tokens: 256 blocks per gate/up row take two passes of the lanes, which
+    sends q > 1 to the general gate/up kernel."""
+    spec = gen.LayerSpec.tiny(hidden=8192, inter=512, n_experts=8, topk=2, rot_down=1)
+    dl = qm.device.DeviceLayer(spec, seed=18)
+    x = gen.tokens(q, spec.hidden, seed=180 + q)
+    out, _ = run_decode(dl, x)
+    ref, _, _ = moe.moe_tokens(oracle_layer(spec, 18, dl.w_router_host), x)
+    assert moe.rel_l2(out, ref) < TOL
+
+
 @pytest.mark.parametrize("ntok,E,hidden", [(16, 40, 256), (100, 256, 768), (33, 300, 512), (64, 512, 1024)])
 def test_route_tiled_logits_bit_exact(ntok, E, hidden):
     """The many-token router (32 x 32 logit tiles, depth-first tree) gives the

@@ -77,6 +77,20 @@ def test_prefill_formats(fmts):
     assert moe.rel_l2(out, ref) < TOL
 
 
+def test_prefill_hidden_8192():
+    """The largest hidden size: 32 K-stages in the gate/up GEMM, 64 row tiles of
+    128 in the down GEMM, and the tiled router's deepest tree."""
+    spec = gen.LayerSpec.tiny(hidden=8192, inter=512, n_experts=8, topk=2)
+    dl = qm.device.DeviceLayer(spec, seed=48)
+    x = gen.tokens(70, spec.hidden, seed=48)
+    out, ws = run_prefill(dl, x)
+    ref, idx_ref, _ = moe.moe_grouped(oracle_layer(spec, 48, dl.w_router_host), x)
+    assert moe.rel_l2(out, ref) < TOL
+    lay = qm.qmoe_workspace_layout(dl.desc, 70)
+    idx = ws[lay["idx"]: lay["idx"] + 4 * 70 * spec.topk].cpu().numpy().view(np.int32).reshape(70, spec.topk)
+    assert np.array_equal(idx, idx_ref)
+
+
 def test_prefill_skewed_many_experts():
     """Zipf-biased routing over 40 experts, top-6: several tiles for the hot
     experts, idle experts, a ragged tail in each."""
