@@ -423,81 +423,102 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 // Top-k of one row of E fp64 logits (E <= 512, K <= 8) by one wave; lane l holds
-// logits l, l+64, ... as order keys. Each of the K rounds first finds the largest
-// high word of the remaining keys; when exactly one key carries it, that key is
-// the maximum. Otherwise the candidates sharing the high word are compared on the
-// full 64-bit key and the lowest id among equal keys wins (the oracle's tie
-// rule). Lane k < K ends with the k-th pick: its id, its key and its rank among
-// the picks in ascending id order (lanes >= K: id 0x7FFFFFFF, key 0, rank 8).
-// Returns the key of the first pick, the largest logit. The row is read with
-// plain loads: it must have been written by an earlier launch.
+// logits l, l+64, ... as order keys and first sorts them (descending key, then
+// ascending id: the oracle's pick order, ties to the lower id). Each of the K
+// rounds then looks only at the lanes' heads: the largest high word among them;
+// when exactly one head carries it, that head is the maximum. Otherwise the
+// heads sharing the high word are compared on the low word, and among equal
+// keys the lowest id wins. The winning lane advances to its next key. Lane
+// k < K ends with the k-th pick: its id, its key and its rank among the picks in
+// ascending id order (lanes >= K: id 0x7FFFFFFF, key 0, rank 8). Returns the key
+// of the first pick, the largest logit. The row is read with plain loads: it
+// must have been written by an earlier launch.
 struct TopkPick {
   int id;
   uint64_t key;
   int rank;
 };
 
+// (key, id) ordered for picking: a before b when a.key > b.key, or the keys are
+// equal and a.id < b.id.
+__device__ __forceinline__ void topk_cas(uint64_t& ka, int& ia, uint64_t& kb, int& ib) {
+  const bool swap = kb > ka || (kb == ka && ib < ia);
+  const uint64_t k = swap ? kb : ka;
+  const int i = swap ? ib : ia;
+  kb = swap ? ka : kb;
+  ib = swap ? ia : ib;
+  ka = k;
+  ia = i;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, v, 0xB1, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, v, 0x4E, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, v, 0x141, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, v, 0x140, 0xF, 0xF, false));
+  const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane(v, 0), (uint32_t)__builtin_amdgcn_readlane(v, 16));
+  const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane(v, 32), (uint32_t)__builtin_amdgcn_readlane(v, 48));
+  return min(a, b);
+}
+
 // NS = slots per lane (E <= 64 * NS); keys of ids >= E are 0 and never win.
 template <int NS>
 __device__ __forceinline__ uint64_t topk_select_ns(const double* __restrict__ row, int E, int K, int lane,
                                                    TopkPick& p) {
   uint64_t key[NS];
+  int id[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const int e = lane + 64 * j;
     key[j] = (e < E) ? f64_order_key(row[e]) : 0;   // key 0: no candidate (no real logit maps to 0)
+    id[j] = e;
   }
+  // sort the lane's slots into pick order (odd-even transposition: NS rounds)
+#pragma unroll
+  for (int r = 0; r < NS; ++r)
+#pragma unroll
+    for (int j = r & 1; j + 1 < NS; j += 2) topk_cas(key[j], id[j], key[j + 1], id[j + 1]);
   p.id = 0x7FFFFFFF;
   p.key = 0;
   uint64_t first = 0;
+  int ptr = 0;   // the lane's next unpicked slot (NS: none left)
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     if (k >= K) break;
-    uint32_t lh = 0;
+    uint64_t hk = 0;
+    int hi_d = 0x7FFFFFFF;
 #pragma unroll
-    for (int j = 0; j < NS; ++j) lh = max(lh, (uint32_t)(key[j] >> 32));
-    const uint32_t gh = wave_max_u32(lh);
-    // this lane's candidates: keys whose high word is the maximum
-    int cs = -1, cnt = 0;
-    uint32_t clo = 0;
-#pragma unroll
-    for (int j = NS - 1; j >= 0; --j)
-      if ((uint32_t)(key[j] >> 32) == gh) {
-        cs = j;
-        clo = (uint32_t)key[j];
-        ++cnt;
+    for (int j = 0; j < NS; ++j)
+      if (j == ptr) {
+        hk = key[j];
+        hi_d = id[j];
       }
-    const uint64_t b = __ballot(cs >= 0);
-    const uint64_t multi = __ballot(cnt > 1);
-    int pick;
-    uint64_t gk;
-    if (multi == 0 && __popcll(b) == 1) {   // one candidate: it is the maximum
-      const int L = (int)__builtin_ctzll(b);
-      pick = 64 * __builtin_amdgcn_readlane(cs, L) + L;
-      gk = ((uint64_t)gh << 32) | (uint32_t)__builtin_amdgcn_readlane(clo, L);
-    } else {   // equal high words: compare full keys, lowest id among equal keys
-      uint64_t lk = 0;
-#pragma unroll
-      for (int j = 0; j < NS; ++j)
-        if ((uint32_t)(key[j] >> 32) == gh) lk = key[j] > lk ? key[j] : lk;
-      gk = wave_max_u64(lk);
-      pick = 0x7FFFFFFF;
-#pragma unroll
-      for (int j = NS - 1; j >= 0; --j) {
-        const uint64_t m = __ballot(key[j] == gk);
-        if (m) pick = 64 * j + (int)__builtin_ctzll(m);
+    const uint32_t hh = (uint32_t)(hk >> 32), hl = (uint32_t)hk;
+    const uint32_t gh = wave_max_u32(hh);
+    const uint64_t b = __ballot(hh == gh);
+    int L;
+    uint32_t gl;
+    if (__popcll(b) == 1) {   // one head carries the largest high word
+      L = (int)__builtin_ctzll(b);
+      gl = (uint32_t)__builtin_amdgcn_readlane(hl, L);
+    } else {
+      gl = wave_max_u32(hh == gh ? hl : 0u);
+      const uint64_t b2 = __ballot(hh == gh && hl == gl);
+      if (__popcll(b2) == 1) {
+        L = (int)__builtin_ctzll(b2);
+      } else {   // equal keys: the lowest id
+        const uint32_t mid = wave_min_u32((hh == gh && hl == gl) ? (uint32_t)hi_d : 0xFFFFFFFFu);
+        L = (int)__builtin_ctzll(__ballot((hh == gh && hl == gl) && (uint32_t)hi_d == mid));
       }
     }
+    const int pick = __builtin_amdgcn_readlane(hi_d, L);
+    const uint64_t gk = ((uint64_t)gh << 32) | gl;
     if (k == 0) first = gk;
     if (lane == k) {
       p.id = pick;
       p.key = gk;
     }
-    if ((pick & 63) == lane) {
-#pragma unroll
-      for (int j = 0; j < NS; ++j)
-        if (j == (pick >> 6)) key[j] = 0;
-    }
+    if (lane == L) ++ptr;
   }
   // rank in ascending id order: the number of picks with a smaller id
   int r = 0;
