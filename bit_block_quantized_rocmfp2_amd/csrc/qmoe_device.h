@@ -417,9 +417,11 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xF, 0xF, true));
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x141, 0xF, 0xF, true));
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x140, 0xF, 0xF, true));
-  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane(v, 0), (uint32_t)__builtin_amdgcn_readlane(v, 16));
-  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane(v, 32), (uint32_t)__builtin_amdgcn_readlane(v, 48));
-  return max(a, b);
+  // row_bcast:15 into rows 1 and 3, then row_bcast:31 into rows 2 and 3: the
+  // last lane holds the wave's maximum (one readlane instead of four)
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(v, v, 0x142, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(v, v, 0x143, 0xC, 0xF, false));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Top-k of one row of E fp64 logits (E <= 512, K <= 8) by one wave; lane l holds
@@ -456,9 +458,9 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, v, 0x4E, 0xF, 0xF, false));
   v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, v, 0x141, 0xF, 0xF, false));
   v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0xFFFFFFFFu, v, 0x140, 0xF, 0xF, false));
-  const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane(v, 0), (uint32_t)__builtin_amdgcn_readlane(v, 16));
-  const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane(v, 32), (uint32_t)__builtin_amdgcn_readlane(v, 48));
-  return min(a, b);
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(v, v, 0x142, 0xA, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(v, v, 0x143, 0xC, 0xF, false));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // NS = slots per lane (E <= 64 * NS); keys of ids >= E are 0 and never win.
@@ -511,7 +513,9 @@ __device__ __forceinline__ uint64_t topk_select_ns(const double* __restrict__ ro
         L = (int)__builtin_ctzll(__ballot((hh == gh && hl == gl) && (uint32_t)hi_d == mid));
       }
     }
-    const int pick = __builtin_amdgcn_readlane(hi_d, L);
+    // the ballots above hold at least one lane by construction; the clamp keeps
+    // an id that addresses expert tensors inside [0, E) regardless
+    const int pick = min(max(__builtin_amdgcn_readlane(hi_d, L), 0), E - 1);
     const uint64_t gk = ((uint64_t)gh << 32) | gl;
     if (k == 0) first = gk;
     if (lane == k) {
