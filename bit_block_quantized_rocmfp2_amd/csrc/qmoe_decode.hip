@@ -79,26 +79,52 @@ struct DecodeArgs {
 };
 
 // ------------------------------------------------------------ k_route
+// One workgroup per expert, two waves per token. The logit is the R6 tree over
+// the row's blocks: lane l holds blocks l + 64c (c < C = P2 / 64), the in-lane
+// levels add s[c] + s[c + n] for n = C/2 .. 1, then xor butterflies over the
+// lanes. With C >= 2 the two waves of a token take c = h and h + 2 (h = wave
+// parity): the in-lane level n = 2 stays in a lane, the level n = 1 (s[0] + s[1])
+// is added across the waves through LDS in the same order, and wave h = 0 runs
+// the butterflies. Each wave issues half the fp64 work of a one-wave router.
+// With C = 1 (hidden <= 2048) the first wave does all of it.
 template <int Q>
-__global__ __launch_bounds__(64 * Q) void k_route(DecodeArgs a) {
-  // wave t computes expert e's logit for token t (one wave per token)
-  const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+__global__ __launch_bounds__(128 * Q) void k_route(DecodeArgs a) {
+  __shared__ double s_half[Q][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = w >> 1, h = w & 1;
   const int e = blockIdx.x;
-  double lg[1];
-  router_wave<1>(a.w_router, a.x + (size_t)t * a.hidden, 1, a.hidden, a.bias, e, 0, lane, lg);
-  if (lane == 0 && t < a.q) a.logits[(size_t)t * a.E + e] = lg[0];
+  const int H = a.hidden, nb = a.nb_h;
+  int P2 = 1;
+  while (P2 < nb) P2 <<= 1;
+  const int C = P2 > 64 ? P2 / 64 : 1;
+  const float* xt = a.x + (size_t)t * H;
+  if (C >= 2) {
+    double v = router_block_sum(a.w_router, xt, H, e, lane + 64 * h, nb);
+    if (C == 4) v = v + router_block_sum(a.w_router, xt, H, e, lane + 64 * (h + 2), nb);
+    if (h == 1) s_half[t][lane] = v;
+    __syncthreads();
+    if (h == 0) {
+      v = v + s_half[t][lane];
+      for (int m = 32; m >= 1; m >>= 1) v = v + __shfl_xor(v, m);
+      if (lane == 0) a.logits[(size_t)t * a.E + e] = a.bias ? v + a.bias[e] : v;
+    }
+  } else if (h == 0) {
+    double lg[1];
+    router_wave<1>(a.w_router, xt, 1, H, a.bias, e, 0, lane, lg);
+    if (lane == 0) a.logits[(size_t)t * a.E + e] = lg[0];
+  }
   // this workgroup's share of the int8 token quantization: two blocks per wave
   // pass, one per half-wave
-  const int nblk = a.q * a.nb_h;
+  const int nblk = a.q * nb;
   const int b_end = min((int)(blockIdx.x + 1) * a.quant_per_wg, nblk);
-  for (int b0 = blockIdx.x * a.quant_per_wg + 2 * t; b0 < b_end; b0 += 2 * Q) {
+  for (int b0 = blockIdx.x * a.quant_per_wg + 2 * w; b0 < b_end; b0 += 4 * Q) {
     const int b = b0 + (lane >> 5), j = lane & 31;
     const bool ok = b < b_end;
     const float v = ok ? a.x[(size_t)b * 32 + j] : 0.0f;
     float d;
-    const uint32_t w = quant_block32_lanes(v, a.rot_gateup, &d);
+    const uint32_t qw = quant_block32_lanes(v, a.rot_gateup, &d);
     if (ok) {
-      if ((j & 3) == 0) reinterpret_cast<uint32_t*>(a.xq + (size_t)b * 32)[j >> 2] = w;
+      if ((j & 3) == 0) reinterpret_cast<uint32_t*>(a.xq + (size_t)b * 32)[j >> 2] = qw;
       if (j == 0) a.dx[b] = d;
     }
   }
@@ -757,7 +783,7 @@ __global__ __launch_bounds__(256) void k_down1(DecodeArgs a) {
 template <int FG, int FD, int Q>
 int launch_decode_t(const DecodeArgs& a, int U_max, hipStream_t s) {
   {
-    launch_kernel("route", k_route<Q>, dim3(a.E), dim3(64 * Q), s, a);
+    launch_kernel("route", k_route<Q>, dim3(a.E), dim3(128 * Q), s, a);
   }
   int st = launch_check("route");
   if (st) return st;

@@ -309,6 +309,34 @@ __device__ __forceinline__ uint32_t quant_block32_lanes(float v, int rot, float*
 // tok/s on AMD Strix Halo", section "Run with Lucebox Engine").
 constexpr int kRouterMaxC = 4;   // blocks per lane: hidden <= 32 * 64 * 4 = 8192
 
+// Sequential fp64 sum of the 32 exact products of block b of expert e's fp16
+// router row and the token x (0 for padding blocks b >= nb).
+__device__ __forceinline__ double router_block_sum(const uint16_t* __restrict__ W, const float* __restrict__ x,
+                                                   int H, int e, int b, int nb) {
+  if (b >= nb) return 0.0;
+  const u32x4* wp = reinterpret_cast<const u32x4*>(W + (size_t)e * H + (size_t)b * 32);
+  uint32_t wv[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 u = wp[i];
+    wv[4 * i] = u.x; wv[4 * i + 1] = u.y; wv[4 * i + 2] = u.z; wv[4 * i + 3] = u.w;
+  }
+  const float4* xp = reinterpret_cast<const float4*>(x + (size_t)b * 32);
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 f = xp[i];
+    const float xs[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int j = 4 * i + k;
+      const uint32_t hb = (j & 1) ? (wv[j >> 1] >> 16) : (wv[j >> 1] & 0xFFFFu);
+      acc = fma((double)half_bits_to_float(hb), (double)xs[k], acc);
+    }
+  }
+  return acc;
+}
+
 // On return every lane holds the logits of tokens t0..t0+TT-1 in out[] (bias
 // included; entries for tokens >= ntok are undefined).
 template <int TT>

@@ -222,6 +222,22 @@ def test_route_hidden_8192(ntok):
         assert moe.rel_l2(out, ref) < TOL
 
 
+@pytest.mark.parametrize("hidden", [2048, 4096, 8192])
+@pytest.mark.parametrize("q", [1, 3])
+def test_decode_logits_bit_exact(hidden, q):
+    """The decode router's fp64 logits (one wave per token for 64 blocks per row
+    or fewer; two waves, with the lowest in-lane tree level added across them,
+    for 128 and 256) equal the oracle's bit for bit."""
+    spec = gen.LayerSpec.tiny(hidden=hidden, n_experts=24, topk=4)
+    bias = gen.zipf_bias(24)
+    dl = qm.device.DeviceLayer(spec, seed=19, bias=bias)
+    x = gen.tokens(q, spec.hidden, seed=190 + q)
+    _, ws = run_decode(dl, x)
+    lay = qm.qmoe_workspace_layout(dl.desc, q)
+    lg = ws[lay["logits"]: lay["logits"] + q * 24 * 8].cpu().numpy().view(np.float64).reshape(q, 24)
+    assert np.array_equal(lg, router.logits(dl.w_router_host, x, bias))
+
+
 @pytest.mark.parametrize("q", [2, 4])
 def test_decode_hidden_8192(q):
     """The largest hidden size through the whole decode layer with several
