@@ -401,10 +401,11 @@ __device__ __forceinline__ void router_wave(const uint16_t* __restrict__ W, cons
 // ---------------------------------------------------------------------------
 // Top-k of one token's E logits (one wave, K <= 8, E <= 512). Equal logits go
 // to the lower id. Logits are compared as order-preserving 64-bit keys (-0.0
-// folded into +0.0 so that equal values tie). A selection round reduces only the
-// 32-bit high words across the wave (DPP exchanges inside 16-lane rows, then the
-// four row maxima); the full keys are compared only when several candidates
-// share the largest high word.
+// folded into +0.0 so that equal values tie). Each lane sorts its keys once; a
+// selection round reduces only the 32-bit high words of the lanes' heads across
+// the wave (DPP exchanges inside 16-lane rows, then row broadcasts); the low
+// words and ids are compared only when several heads share the largest high
+// word.
 constexpr int kTopkMaxPerLane = 8;   // E <= 512
 
 __device__ __forceinline__ uint64_t f64_order_key(double v) {
