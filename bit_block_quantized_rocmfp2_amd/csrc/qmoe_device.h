@@ -406,7 +406,6 @@ __device__ __forceinline__ void router_wave(const uint16_t* __restrict__ W, cons
 // the wave (DPP exchanges inside 16-lane rows, then row broadcasts); the low
 // words and ids are compared only when several heads share the largest high
 // word.
-constexpr int kTopkMaxPerLane = 8;   // E <= 512
 
 __device__ __forceinline__ uint64_t f64_order_key(double v) {
   if (v == 0.0) v = 0.0;   // -0.0 -> +0.0
@@ -417,26 +416,6 @@ __device__ __forceinline__ uint64_t f64_order_key(double v) {
 __device__ __forceinline__ double f64_from_order_key(uint64_t k) {
   const uint64_t b = (k >> 63) ? (k ^ 0x8000000000000000ull) : ~k;
   return __longlong_as_double((long long)b);
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, 0xF, 0xF, true);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  uint64_t o;
-  o = dpp_u64<0xB1>(v);  v = o > v ? o : v;    // quad_perm [1,0,3,2]: lane ^ 1
-  o = dpp_u64<0x4E>(v);  v = o > v ? o : v;    // quad_perm [2,3,0,1]: lane ^ 2
-  o = dpp_u64<0x141>(v); v = o > v ? o : v;    // row_half_mirror: quads 0 <-> 1 of each 8
-  o = dpp_u64<0x140>(v); v = o > v ? o : v;    // row_mirror: halves of each 16-lane row
-  o = ((uint64_t)(uint32_t)__shfl_xor((int)(v >> 32), 16) << 32) | (uint32_t)__shfl_xor((int)(uint32_t)v, 16);
-  v = o > v ? o : v;
-  o = ((uint64_t)(uint32_t)__shfl_xor((int)(v >> 32), 32) << 32) | (uint32_t)__shfl_xor((int)(uint32_t)v, 32);
-  v = o > v ? o : v;
-  return v;
 }
 
 // Wave-wide maximum of a uint32 (uniform result): four DPP exchanges give every
