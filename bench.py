@@ -219,6 +219,39 @@ def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
     log(f"decode q=4: {ms * 1e3:.2f} us/call, U={np.mean(U):.2f}, {gbs:.1f} GB/s; kernels (us): "
         + ", ".join(f"{k}={v}" for k, v in kern.items()))
 
+    # ablation: the same four columns decoded one call per column (each expert
+    # block decoded once per routed column instead of once per group)
+    cols = [[g[t:t + 1] for t in range(4)] for g in groups]
+    for i in range(10):
+        for t in range(4):
+            qm.qmoe_decode_layer(dl.desc, cols[i % len(groups)][t], out[t:t + 1], ws)
+    with Timer(torch) as t_pc:
+        for i in range(K):
+            for t in range(4):
+                qm.qmoe_decode_layer(dl.desc, cols[i % len(groups)][t], out[t:t + 1], ws)
+    ms_pc = t_pc.ms / K
+    res["decode_q4_per_column"] = {"us_per_4_tokens": round(ms_pc * 1e3, 2),
+                                   "tokens_per_s": round(4 / (ms_pc * 1e-3), 1),
+                                   "decode_once_speedup": round(ms_pc / ms, 3),
+                                   "packed_bytes_read": 4 * spec.topk * per_expert}
+    log(f"decode q=4 as four q=1 calls: {ms_pc * 1e3:.2f} us ({ms_pc / ms:.2f}x the decode-once call)")
+
+    # routing variant: the same layer with top-4 routing, q = 1
+    desc4 = qm.make_layer(spec.hidden, spec.inter, spec.n_experts, 4, spec.fmt_gate, spec.fmt_up, spec.fmt_down,
+                          spec.rot_gateup, spec.rot_down, dl.w_router, None, dl.gate, dl.up, dl.down, dl.cb_gate,
+                          dl.cb_up, dl.cb_down)
+    toks = torch.from_numpy(gen.tokens(64, spec.hidden, seed=0, stream=7)).to(dev)
+    for i in range(10):
+        qm.qmoe_decode_layer(desc4, toks[i % 64: i % 64 + 1], out[:1], ws)
+    with Timer(torch) as t4:
+        for i in range(K):
+            qm.qmoe_decode_layer(desc4, toks[i % 64: i % 64 + 1], out[:1], ws)
+    ms4 = t4.ms / K
+    gbs4 = 4 * per_expert / (ms4 * 1e-3) / 1e9
+    res["decode_q1_top4"] = {"us_per_call": round(ms4 * 1e3, 2), "effective_GBps": round(gbs4, 1),
+                             "frac_hbm_peak": round(gbs4 / HBM_PEAK_GBS, 4)}
+    log(f"decode q=1 top-4: {ms4 * 1e3:.2f} us/call, {gbs4:.1f} GB/s")
+
     # ---------------------------------------------------------------- prefill 8K (Zipf)
     try:
         res["prefill_8k"] = bench_prefill(torch, qm, gen, spec, dl, dev)

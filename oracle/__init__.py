@@ -31,4 +31,4 @@ against hand-worked values, closed forms, exact rational arithmetic, brute
 force on tiny inputs or a public specification (OCP MX FP4). No function is
 "parity unpinned".
 """
-from . import formats, quant, hadamard, dots, router, moe  # noqa: F401
+from . import formats, quant, hadamard, dots, router, moe, quantize  # noqa: F401

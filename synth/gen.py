@@ -30,13 +30,14 @@ __all__ = [
     "rng", "uniform_codes", "fp16_scales", "e8m0_scales", "codebook",
     "MatvecCase", "fp2_matvec", "matvec_case", "LayerSpec", "ExpertTensor",
     "expert_tensor", "router_weights", "tokens", "zipf_bias", "q4_group",
-    "dense_mix", "STREAM",
+    "dense_mix", "float_matrices", "STREAM",
 ]
 
 # Stream ids keep the draws of different tensors independent of each other.
 STREAM = {
     "gate": 11, "up": 12, "down": 13, "router": 14, "tokens": 15, "q4": 16,
     "matvec": 17, "dense_fp4": 18, "dense_fp3": 19, "dense_x": 20,
+    "float_w": 21,
 }
 
 
@@ -193,3 +194,18 @@ def dense_mix(ncols: int = 1, seed: int = 0):
     fp4 = matvec_case(4, 4096, 16384, ncols, seed, rot=0, stream=STREAM["dense_fp4"])
     fp3 = matvec_case(3, 4096, 2048, ncols, seed, rot=1, stream=STREAM["dense_fp3"])
     return fp4, fp3
+
+
+def float_matrices(n: int, rows: int, k: int, seed: int = 0, sigma: float = 0.02,
+                   outlier_frac: float = 1e-3) -> np.ndarray:
+    """fp32 weights [n, rows, k] to quantize: N(0, sigma) with a fraction of
+    outliers drawn N(0, 10 sigma) (heavy-tailed like trained projection weights);
+    matrix m is drawn from its own stream, so any one can be regenerated alone."""
+    out = np.empty((n, rows, k), dtype=np.float32)
+    for m in range(n):
+        g = rng(seed, STREAM["float_w"], m, rows, k)
+        w = g.standard_normal((rows, k)) * sigma
+        mask = g.random((rows, k)) < outlier_frac
+        w[mask] *= 10.0
+        out[m] = w.astype(np.float32)
+    return out

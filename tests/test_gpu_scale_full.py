@@ -66,6 +66,28 @@ def test_full_decode_q1(full):
         assert err < TOL
 
 
+def test_full_decode_q1_top4(full):
+    """The same full layer routed top-4 (a routing variant of the layer): ids
+    bit-exact, output within the tolerance, q = 1 and q = 4."""
+    spec, dl, L6 = full
+    desc4 = qm.make_layer(spec.hidden, spec.inter, spec.n_experts, 4, spec.fmt_gate, spec.fmt_up, spec.fmt_down,
+                          spec.rot_gateup, spec.rot_down, dl.w_router, None, dl.gate, dl.up, dl.down, dl.cb_gate,
+                          dl.cb_up, dl.cb_down)
+    L4 = moe.Layer(spec.hidden, spec.inter, spec.n_experts, 4, dl.w_router_host, L6.get)
+    for q in (1, 4):
+        x = gen.tokens(q, spec.hidden, seed=SEED + 4, stream=3)
+        xd = qm.device.to_device(x)
+        out = torch.empty_like(xd)
+        ws = torch.zeros(qm.qmoe_workspace_bytes(desc4, q), dtype=torch.uint8, device="cuda")
+        qm.qmoe_decode_layer(desc4, xd, out, ws)
+        torch.cuda.synchronize()
+        lay = qm.qmoe_workspace_layout(desc4, q)
+        idx = ws[lay["idx"]: lay["idx"] + q * 4 * 4].cpu().numpy().view(np.int32).reshape(q, 4)
+        ref, idx_ref, _ = moe.moe_tokens(L4, x)
+        assert np.array_equal(idx, idx_ref)
+        assert moe.rel_l2(out.cpu().numpy(), ref) < TOL
+
+
 def test_full_decode_q4_forced_overlap(full):
     spec, dl, L = full
     for variant in range(64):
