@@ -81,6 +81,9 @@ def _load():
         "qmoe_quant_act": (c_int, [c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
         "qmoe_block_dots": (c_int, [c_int, c_int64, c_int64, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p,
                                     c_void_p]),
+        "qmoe_quantize_workspace_bytes": (c_size_t, [c_int32, c_int64, c_int64]),
+        "qmoe_quantize": (c_int, [c_int, c_int32, c_int64, c_int64, c_void_p, c_int32, c_void_p, c_size_t, c_void_p,
+                                  c_void_p, c_size_t, c_void_p]),
         "qmoe_timing_enable": (c_int, [c_int]),
         "qmoe_timing_read": (c_int, [c_char_p, POINTER(c_double), POINTER(c_int)]),
     }
@@ -97,7 +100,7 @@ EXPORTED = (
     "qmoe_strerror", "qmoe_last_error", "qmoe_version", "qmoe_block_bytes", "qmoe_packed_bytes", "qmoe_pack",
     "qmoe_unpack", "qmoe_layer_check", "qmoe_workspace_bytes", "qmoe_workspace_layout", "qmoe_route",
     "qmoe_decode_layer", "qmoe_prefill_layer", "qmoe_matvec_workspace_bytes", "qmoe_matvec", "qmoe_quant_act",
-    "qmoe_block_dots", "qmoe_timing_enable", "qmoe_timing_read",
+    "qmoe_block_dots", "qmoe_quantize_workspace_bytes", "qmoe_quantize", "qmoe_timing_enable", "qmoe_timing_read",
 )
 
 
@@ -227,6 +230,17 @@ def qmoe_quant_act(x, rot, xq, dx, stream=None) -> None:
 def qmoe_block_dots(fmt, rows, k, w, cb, xq, P, stream=None) -> None:
     _check(LIB.qmoe_block_dots(fmt, rows, k, _ptr(w), _nbytes(w), _ptr(cb), _ptr(xq), _ptr(P), _stream(stream)),
            "qmoe_block_dots")
+
+
+def qmoe_quantize_workspace_bytes(n: int, rows: int, k: int) -> int:
+    return LIB.qmoe_quantize_workspace_bytes(n, rows, k)
+
+
+def qmoe_quantize(fmt, w, iters, out, cb, ws, stream=None) -> None:
+    """w: fp32 [n, rows, k]; out: uint8 [n, rows, row_bytes]; cb: int8 [n, 2^bits]."""
+    n, rows, k = w.shape
+    _check(LIB.qmoe_quantize(fmt, n, rows, k, _ptr(w), iters, _ptr(out), _nbytes(out), _ptr(cb), _ptr(ws),
+                             _nbytes(ws), _stream(stream)), "qmoe_quantize")
 
 
 def qmoe_timing_enable(on: bool) -> None:

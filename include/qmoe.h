@@ -186,6 +186,29 @@ typedef struct {
 
 int qmoe_workspace_layout(const qmoe_layer* L, int32_t max_tokens, qmoe_ws_layout* out);
 
+/* Weight quantizer: n fp32 matrices w [n][rows][k] (device, 16-byte aligned,
+ * finite) -> packed ROCmFPX rows out [n][rows][row_bytes] (device) and one int8
+ * codebook per matrix cb [n][2^bits] (device). The pages say the expert
+ * weights carry learned codebooks, one per expert ([0731-Strix], section "How
+ * the model fits on AMD Strix Halo"), in 32-weight blocks with a small scale
+ * ([Strix-284B], ROCmFPX section); the procedure is the format specification's
+ * weight-quantization section: per block an absmax scale (fp16 for FP2/FP3, a
+ * power of two E8M0 for FP4), the weights normalized to integers in units of
+ * scale/256, `iters` (0..64) Lloyd iterations of a 1-D k-means per matrix in
+ * integer arithmetic (results independent of reduction order), then the
+ * nearest codebook entry of each weight (ties to the lower entry).
+ * k: a multiple of 256 (FP2/FP3) or 512 (FP4). ws: caller-owned device
+ * workspace of qmoe_quantize_workspace_bytes(n, rows, k) bytes, 256-byte
+ * aligned; its contents need no initialisation and are scratch afterwards.
+ * Asynchronous on `stream`; never allocates or synchronises. Errors (checked
+ * before any launch): QMOE_E_FORMAT, QMOE_E_SHAPE (k, iters, sizes),
+ * QMOE_E_INVAL (NULL or misaligned pointers), QMOE_E_SIZE (out too small),
+ * QMOE_E_WORKSPACE. */
+size_t qmoe_quantize_workspace_bytes(int32_t n, int64_t rows, int64_t k);
+int qmoe_quantize(qmoe_format f, int32_t n, int64_t rows, int64_t k, const float* w,
+                  int32_t iters, void* out, size_t out_bytes, int8_t* cb, void* ws,
+                  size_t ws_bytes, void* stream);
+
 /* Kernel timing (instrumentation). qmoe_timing_enable(1) starts recording, for
  * every kernel that an entry point launches afterwards, a pair of HIP events
  * carried by the kernel's own dispatch (so the elapsed time is the kernel's
@@ -194,7 +217,8 @@ int qmoe_workspace_layout(const qmoe_layer* L, int32_t max_tokens, qmoe_ws_layou
  * their summed time in ms and their count. Names: "quant_act", "router",
  * "topk", "matvec" (shared); "route", "gateup", "down" (decode);
  * "group_count", "group_scan", "group_scatter", "gateup_mfma", "down_mfma",
- * "combine" (prefill). */
+ * "combine" (prefill); "qz_norm", "qz_assign", "qz_update", "qz_pack"
+ * (quantizer). */
 int qmoe_timing_enable(int on);
 int qmoe_timing_read(const char* name, double* total_ms, int* count);
 

@@ -25,8 +25,8 @@ def block_scales(fmt: int, w: np.ndarray):
     """Q1. w float32 [..., K] -> (stored scale, d float32) per 32-block.
 
     FP2/FP3 store fp16 bits h = fp16_rne(fl32(amax / 127)), saturated to 65504;
-    FP4 stores E8M0 e with 2^(e-127) the least power of two >= fl32(amax / 127)
-    (e = 0 for an all-zero block), clamped to 0..254."""
+    FP4 stores E8M0 e with 2^(e-127) the least power of two >= fl32(amax / 127),
+    clamped to 1..254 (e = 0 only for an all-zero block)."""
     w = np.asarray(w, dtype=np.float32)
     blocks = w.reshape(*w.shape[:-1], w.shape[-1] // BLOCK, BLOCK)
     a = np.max(np.abs(blocks), axis=-1).astype(np.float32)
@@ -39,13 +39,14 @@ def block_scales(fmt: int, w: np.ndarray):
     # FP4: t = m * 2^x with m in [0.5, 1); t is a power of two exactly when m = 0.5
     m, x = np.frexp(t.astype(np.float64))
     k = np.where(m == 0.5, x - 1, x)                       # least k with 2^k >= t
-    e = np.where(t > 0, np.clip(127 + k, 0, 254), 0).astype(np.int64)
+    e = np.where(t > 0, np.clip(127 + k, 1, 254), 0).astype(np.int64)
     d = np.ldexp(np.float64(1.0), e - 127).astype(np.float32)   # exact (2^-127 is an fp32 subnormal)
     return e.astype(np.uint8), d
 
 
 def normalized(w: np.ndarray, d: np.ndarray) -> np.ndarray:
-    """Q2. v = clamp(rne(fl32(w / d) * 256), -32767, 32767), 0 where d = 0.
+    """Q2. v = clamp(rne(fl32(w / d) * 256), -32767, 32767), 0 where d = 0 (an
+    all-zero block, amax = 0, gives v = 0 in every format).
     w float32 [..., K], d float32 [..., K/32] -> int64 [..., K]."""
     w = np.asarray(w, dtype=np.float32)
     blocks = w.reshape(*w.shape[:-1], w.shape[-1] // BLOCK, BLOCK)

@@ -207,3 +207,29 @@ def test_launch_entry_points_reject_before_launch():
     assert st == -2
     st = B.LIB.qmoe_prefill_layer(ctypes.byref(L), x.ctypes.data, 4, out.ctypes.data, ws.ctypes.data, 16, None)
     assert st == -6
+
+
+def test_quantize_rejects_bad_arguments_before_launch():
+    """Argument errors of qmoe_quantize are reported on the host, before any
+    device work (host pointers stand in: nothing is launched on these paths)."""
+    w = np.zeros((1, 4, 256), dtype=np.float32)
+    out = np.zeros((1, 4, 80), dtype=np.uint8)
+    cb = np.zeros((1, 4), dtype=np.int8)
+    ws = np.zeros(qm.qmoe_quantize_workspace_bytes(1, 4, 256) + 256, dtype=np.uint8)
+    wsa = ws[(-ws.ctypes.data) % 256:]                     # 256-byte aligned view
+    L = B.LIB
+
+    def call(fmt=2, n=1, rows=4, k=256, wp=w, iters=4, o=out, ob=None, c=cb, wsp=wsa, wsb=None):
+        return L.qmoe_quantize(fmt, n, rows, k, B._ptr(wp), iters, B._ptr(o), o.nbytes if ob is None else ob,
+                               B._ptr(c), B._ptr(wsp), wsp.nbytes if wsb is None else wsb, None)
+    assert call(fmt=5) == -3                               # unknown format
+    assert call(k=96) == -2                                # row not a multiple of 16 bytes
+    assert call(k=100) == -2                               # not a multiple of 32
+    assert call(iters=65) == -2 and call(iters=-1) == -2
+    assert call(n=0) == -2
+    assert call(wp=None) == -1
+    assert call(ob=10) == -8                               # out too small
+    assert call(wsb=100) == -6                             # workspace too small
+    assert call(fmt=4, k=256) == -2                        # FP4 needs k % 512 == 0
+    assert qm.qmoe_quantize_workspace_bytes(1, 4, 33) == 0
+    assert qm.qmoe_quantize_workspace_bytes(2, 2048, 4096) >= 2 * 2048 * 4096 * 2

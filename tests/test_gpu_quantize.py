@@ -1,0 +1,80 @@
+"""GPU parity of the weight quantizer (qmoe_quantize) against the CPU oracle,
+through the C ABI: packed bytes (codes and scales) and the fitted codebooks
+are integer results and must match bit for bit.
+
+Cases: ragged tiny shapes in all three formats at 0, 1 and 6 Lloyd iterations,
+with a zero block, an outlier, a block whose fp16 scale saturates and one whose
+fp16 scale underflows to zero; more than 16 matrices (the centroid start of the
+later matrices is written by a second kernel); full-size expert matrices
+(gate/up FP2 2048x4096, down FP3 4096x2048) and an FP4 1024x16384 slice of the
+dense projection, at the iteration count the benchmark times; and repeated
+calls on one workspace being identical.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+import bit_block_quantized_rocmfp2_amd as qm  # noqa: E402
+from oracle import formats, quantize  # noqa: E402
+from synth import gen  # noqa: E402
+
+
+def run(fmt, w, iters, ws=None):
+    n, rows, k = w.shape
+    wd = torch.from_numpy(w).cuda()
+    out = torch.zeros((n, rows, formats.row_bytes(fmt, k)), dtype=torch.uint8, device="cuda")
+    cb = torch.zeros((n, 1 << formats.BITS[fmt]), dtype=torch.int8, device="cuda")
+    if ws is None:
+        ws = torch.empty(qm.qmoe_quantize_workspace_bytes(n, rows, k), dtype=torch.uint8, device="cuda")
+    qm.qmoe_quantize(fmt, wd, iters, out, cb, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), cb.cpu().numpy()
+
+
+def tiny_weights(fmt, n, rows, k, seed):
+    w = gen.float_matrices(n, rows, k, seed=seed)
+    w[0, 0, :32] = 0.0                     # zero block
+    w[0, 1, 7] = 0.5                       # outlier
+    w[n - 1, rows - 1, -32:] = 1.0e7       # fp16 scale saturates at 65504 (FP2/FP3)
+    w[n - 1, 0, 32:64] *= 1e-28            # fp16 scale underflows to 0; small E8M0 exponent
+    return w
+
+
+@pytest.mark.parametrize("fmt,k", [(2, 256), (3, 256), (4, 512)])
+@pytest.mark.parametrize("iters", [0, 1, 6])
+def test_quantize_tiny(fmt, k, iters):
+    w = tiny_weights(fmt, 3, 5, k, seed=30 + fmt)
+    packed, cb = run(fmt, w, iters)
+    ref_packed, ref_cb, _, _ = quantize.quantize(fmt, w, iters)
+    assert np.array_equal(cb, ref_cb)
+    assert np.array_equal(packed, ref_packed)
+
+
+def test_quantize_many_matrices():
+    w = gen.float_matrices(20, 3, 256, seed=40)
+    packed, cb = run(3, w, 3)
+    ref_packed, ref_cb, _, _ = quantize.quantize(3, w, 3)
+    assert np.array_equal(cb, ref_cb)
+    assert np.array_equal(packed, ref_packed)
+
+
+@pytest.mark.parametrize("fmt,rows,k,iters", [(2, 2048, 4096, 8), (3, 4096, 2048, 8), (4, 1024, 16384, 4)])
+def test_quantize_full_size(fmt, rows, k, iters):
+    w = gen.float_matrices(1, rows, k, seed=50 + fmt)
+    packed, cb = run(fmt, w, iters)
+    ref_packed, ref_cb, _, _ = quantize.quantize(fmt, w, iters)
+    assert np.array_equal(cb, ref_cb)
+    diff = np.flatnonzero(packed.ravel() != ref_packed.ravel())
+    assert diff.size == 0, (diff.size, diff[:10])
+
+
+def test_quantize_repeat_identical():
+    w = gen.float_matrices(2, 64, 512, seed=60)
+    ws = torch.empty(qm.qmoe_quantize_workspace_bytes(2, 64, 512), dtype=torch.uint8, device="cuda")
+    a = run(2, w, 5, ws)
+    run(2, gen.float_matrices(2, 64, 512, seed=61), 5, ws)   # stale workspace contents in between
+    b = run(2, w, 5, ws)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

@@ -153,7 +153,7 @@ def py_quantize(fmt, w, iters):
                         kk = -200
                         while 2.0 ** kk < float(t):
                             kk += 1
-                        e = min(max(127 + kk, 0), 254)
+                        e = min(max(127 + kk, 1), 254)
                     d = f32(2.0 ** (e - 127))
                     scs[r, b] = e
                 else:
