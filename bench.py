@@ -281,6 +281,9 @@ def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
                                       "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "packed_bytes": nbytes}
         log(f"dense mix q={ncols}: {ms * 1e3:.2f} us, {gbs:.1f} GB/s")
 
+    # ---------------------------------------------------------------- weight quantizer
+    res["quantize_fp2"] = bench_quantize(torch, qm, gen, dev)
+
     # ---------------------------------------------------------------- FP2 512x256 matvec latency
     c = gen.fp2_matvec(0)
     m = qm.device.DeviceMatrix(c)
@@ -293,6 +296,46 @@ def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
         for _ in range(K):
             qm.qmoe_matvec(2, 512, 256, m.w, m.cb, 0, x, y, w)
     res["fp2_matvec_512x256"] = {"us_per_call": round(t.ms / K * 1e3, 2)}
+    return res
+
+
+def bench_quantize(torch, qm, gen, dev, n=16, rows=2048, k=4096, iters=8):
+    """qmoe_quantize on the gate and up matrices of 8 experts (n = 16 fp32
+    2048 x 4096 matrices, N(0, 0.02) with 0.1% outliers), FP2, 8 Lloyd
+    iterations. Algorithmic HBM bytes per weight: norm 4 (fp32 in) + 2 (int16
+    out) + 1/16 (scale); assign 2 per iteration; pack 2 + 1/16 in, 10/32 out."""
+    w = torch.from_numpy(gen.float_matrices(n, rows, k, seed=0)).to(dev)
+    out = torch.empty((n, rows, (k // 32) * 10), dtype=torch.uint8, device=dev)
+    cb = torch.empty((n, 4), dtype=torch.int8, device=dev)
+    ws = torch.empty(qm.qmoe_quantize_workspace_bytes(n, rows, k), dtype=torch.uint8, device=dev)
+    qm.qmoe_quantize(2, w, iters, out, cb, ws)
+    torch.cuda.synchronize()
+    reps = 5
+    with Timer(torch) as t:
+        for _ in range(reps):
+            qm.qmoe_quantize(2, w, iters, out, cb, ws)
+    ms = t.ms / reps
+    qm.qmoe_timing_enable(True)
+    for _ in range(reps):
+        qm.qmoe_quantize(2, w, iters, out, cb, ws)
+    torch.cuda.synchronize()
+    nw = n * rows * k
+    per_w = {"qz_norm": 4 + 2 + 2 / 32, "qz_assign": 2.0, "qz_pack": 2 + 2 / 32 + 10 / 32}
+    kern = {}
+    for name in ("qz_norm", "qz_assign", "qz_update", "qz_pack"):
+        avg, _ = kernel_avg_ms(qm, name)
+        if avg:
+            e = {"us": round(avg * 1e3, 2)}
+            if name in per_w:
+                gbs = per_w[name] * nw / (avg * 1e-3) / 1e9
+                e.update({"GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+            kern[name] = e
+    qm.qmoe_timing_enable(False)
+    res = {"ms_per_call": round(ms, 3), "matrices": n, "shape": [rows, k], "iters": iters,
+           "weights_per_s": round(nw / (ms * 1e-3), 1), "fp32_input_GBps": round(4 * nw / (ms * 1e-3) / 1e9, 1),
+           "kernels": kern}
+    log(f"quantize FP2 {n}x{rows}x{k}, {iters} iters: {ms:.3f} ms; kernels: {kern}")
+    del w, out, ws
     return res
 
 

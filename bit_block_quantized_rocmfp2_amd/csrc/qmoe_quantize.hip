@@ -14,16 +14,18 @@
 // weight; every step after the normalization is integer arithmetic, so the
 // codebook does not depend on the order of any reduction.
 //
-//   k_qz_norm    32 lanes per block: amax by DPP exchanges, the block's stored
-//                scale and divisor, the int16 normalized values v (coalesced);
-//                workgroup 0 also writes the starting centroids.
+//   k_qz_norm    8 lanes per block, 4 weights per lane (16-byte loads): amax
+//                by DPP exchanges, the block's stored scale and divisor, the
+//                int16 normalized values v; workgroup 0 also writes the
+//                starting centroids.
 //   k_qz_assign  one Lloyd assignment pass: G workgroups per matrix stream its
 //                v, each lane keeps per-entry sums and counts in LDS slots of
 //                its own (no contention), and each workgroup writes its integer
 //                partial sums; no atomics.
-//   k_qz_update  one workgroup per matrix: adds the G partials of each entry in
-//                a fixed order and moves the centroid to the mean rounded half
-//                up (floor division); an entry with no members keeps its value.
+//   k_qz_update  one workgroup per matrix: adds the G partials of each entry
+//                (exact integers) and moves the centroid to the mean rounded
+//                half up (floor division); an entry with no members keeps its
+//                value.
 //   k_qz_pack    one thread per block: the int8 codebook from the centroids,
 //                the nearest entry of each weight, packed into the row-planar
 //                layout with the block's scale; the first block of each matrix
@@ -82,21 +84,22 @@ __device__ __forceinline__ int ceil_log2_f32(float t) {
   return (int)ex - 127 + (man ? 1 : 0);
 }
 
-// Q1, Q2: thread g handles weight g of the flattened [n][rows][k]; the 32 lanes
-// of each half-wave hold one block. All lanes take part in the exchanges.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Q1, Q2: thread g handles weights 4g..4g+3 of the flattened [n][rows][k]
+// (one 16-byte load); the 8 lanes of each aligned group of 8 hold one block.
+// All lanes take part in the exchanges.
 template <int FMT>
 __global__ __launch_bounds__(256) void k_qz_norm(const float* __restrict__ w, size_t nw, int n, int16_t* __restrict__ v,
                                                  uint16_t* __restrict__ sc, long long* __restrict__ c) {
 #pragma clang fp contract(off)
   const size_t g = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const bool ok = g < nw;
-  const float x = ok ? w[g] : 0.0f;
-  float m = fabsf(x);
+  const bool ok = 4 * g < nw;
+  const f32x4 x = ok ? reinterpret_cast<const f32x4*>(w)[g] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
   m = fmaxf(m, xchg32<1>(m));
   m = fmaxf(m, xchg32<2>(m));
   m = fmaxf(m, xchg32<4>(m));
-  m = fmaxf(m, xchg32<8>(m));
-  m = fmaxf(m, xchg32<16>(m));
   const float t = m / 127.0f;
   uint32_t stored;
   float d;
@@ -108,14 +111,18 @@ __global__ __launch_bounds__(256) void k_qz_norm(const float* __restrict__ w, si
     stored = (t >= 65520.0f) ? 0x7BFFu : (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)t);
     d = half_bits_to_float(stored);
   }
-  int q = 0;
-  if (m > 0.0f && d > 0.0f) {
-    const float r = rintf((x / d) * 256.0f);
-    q = (int)fminf(fmaxf(r, -32767.0f), 32767.0f);
+  const bool live = m > 0.0f && d > 0.0f;
+  const float xs[4] = {x.x, x.y, x.z, x.w};
+  uint32_t q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int qi = 0;
+    if (live) qi = (int)fminf(fmaxf(rintf((xs[i] / d) * 256.0f), -32767.0f), 32767.0f);
+    q[i] = (uint32_t)qi & 0xFFFFu;
   }
   if (ok) {
-    v[g] = (int16_t)q;
-    if ((threadIdx.x & 31) == 0) sc[g >> 5] = (uint16_t)stored;
+    reinterpret_cast<u32x2*>(v)[g] = u32x2{q[0] | (q[1] << 16), q[2] | (q[3] << 16)};
+    if ((threadIdx.x & 7) == 0) sc[g >> 3] = (uint16_t)stored;
   }
   if (blockIdx.x == 0 && threadIdx.x < n * kQzMaxEntries && threadIdx.x < 256) {
     // starting centroids: midpoints of 2^bits equal cells over [-127, 127]
@@ -149,35 +156,70 @@ __device__ __forceinline__ int qz_nearest(int x, const int (&cc)[NC]) {
   return best;
 }
 
+// Nearest of NC strictly increasing centroids, from their pairwise sums
+// mid[i] = c_i + c_{i+1}: c_{i+1} is strictly nearer than c_i exactly when
+// 2x > mid[i], and the mids increase, so the indicators read 1..1 0..0 and their
+// count is the lowest index of the nearest centroid (ties stay low), the same
+// as qz_nearest.
+template <int NC>
+__device__ __forceinline__ int qz_nearest_sorted(int x, const int (&mid)[NC - 1]) {
+  int a = 0;
+#pragma unroll
+  for (int i = 0; i < NC - 1; ++i) a += (2 * x > mid[i]) ? 1 : 0;
+  return a;
+}
+
+template <int NC, bool SORTED>
+__device__ __forceinline__ void qz_assign_loop(const u32x4* __restrict__ src, size_t npieces, size_t first,
+                                               size_t stride, const int (&cc)[NC], const int (&mid)[NC - 1],
+                                               int (&s_sum)[NC][256], int (&s_cnt)[NC][256]) {
+  const int tid = threadIdx.x;
+  for (size_t p = first; p < npieces; p += stride) {
+    const u32x4 r = src[p];
+    const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      const int x = (int)(int16_t)(wd[h >> 1] >> (16 * (h & 1)));
+      const int a = SORTED ? qz_nearest_sorted<NC>(x, mid) : qz_nearest<NC>(x, cc);
+      // LDS adds without a returned value: no read-modify-write chain between
+      // the values (the slots are this thread's own, in distinct banks per lane)
+      atomicAdd(&s_sum[a][tid], x);
+      atomicAdd(&s_cnt[a][tid], 1);
+    }
+  }
+}
+
 // Q3, assignment: grid (G, n). Lane slots s_sum/s_cnt[entry][thread] hold this
 // thread's sums (at most 8 * 32767 per piece, so int32 is exact per slot up to
-// 2^31 / 32767 = 65538 values per thread) and counts.
+// 2^31 / 32767 = 65538 values per thread) and counts. Lloyd's iterations keep
+// the centroids in order; the pairwise-sum shortcut is taken when they are
+// strictly increasing (checked per workgroup), the full scan otherwise.
 template <int NC>
 __global__ __launch_bounds__(256) void k_qz_assign(const int16_t* __restrict__ v, size_t per_mat,
                                                    const long long* __restrict__ c, long long* __restrict__ part) {
   __shared__ int s_sum[NC][256];
   __shared__ int s_cnt[NC][256];
   const int tid = threadIdx.x, m = blockIdx.y, G = gridDim.x;
-  int cc[NC];
+  int cc[NC], mid[NC - 1];
+  bool inc = true;
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
     cc[i] = (int)c[(size_t)m * kQzMaxEntries + i];
     s_sum[i][tid] = 0;
     s_cnt[i][tid] = 0;
   }
+#pragma unroll
+  for (int i = 0; i < NC - 1; ++i) {
+    mid[i] = cc[i] + cc[i + 1];
+    inc = inc && cc[i] < cc[i + 1];
+  }
   const u32x4* src = reinterpret_cast<const u32x4*>(v + (size_t)m * per_mat);
   const size_t npieces = per_mat / 8;   // 8 values per 16-byte piece
-  for (size_t p = (size_t)blockIdx.x * 256 + tid; p < npieces; p += (size_t)G * 256) {
-    const u32x4 r = src[p];
-    const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-    for (int h = 0; h < 8; ++h) {
-      const int x = (int)(int16_t)(wd[h >> 1] >> (16 * (h & 1)));
-      const int a = qz_nearest<NC>(x, cc);
-      s_sum[a][tid] += x;
-      s_cnt[a][tid] += 1;
-    }
-  }
+  const size_t first = (size_t)blockIdx.x * 256 + tid, stride = (size_t)G * 256;
+  if (inc)
+    qz_assign_loop<NC, true>(src, npieces, first, stride, cc, mid, s_sum, s_cnt);
+  else
+    qz_assign_loop<NC, false>(src, npieces, first, stride, cc, mid, s_sum, s_cnt);
   __syncthreads();
   // per entry: the workgroup's sum and count, then its partial slot
   if (tid < NC) {
@@ -192,22 +234,38 @@ __global__ __launch_bounds__(256) void k_qz_assign(const int16_t* __restrict__ v
   }
 }
 
-// Q3, update: one workgroup per matrix.
-__global__ __launch_bounds__(64) void k_qz_update(long long* __restrict__ c, const long long* __restrict__ part, int G,
-                                                  int nc) {
-  const int m = blockIdx.x, i = threadIdx.x;
-  if (i >= nc) return;
+// Q3, update: one workgroup per matrix; 16 threads per entry each add every
+// 16th partial (all loads in flight at once), then one thread per entry adds
+// the 16 sub-sums in order.
+__global__ __launch_bounds__(256) void k_qz_update(long long* __restrict__ c, const long long* __restrict__ part, int G,
+                                                   int nc) {
+  __shared__ long long sS[kQzMaxEntries][16], sN[kQzMaxEntries][16];
+  const int m = blockIdx.x, i = threadIdx.x >> 4, j = threadIdx.x & 15;
   long long S = 0, N = 0;
-  for (int g = 0; g < G; ++g) {
-    const long long* p = part + (((size_t)m * kQzGroups + g) * kQzMaxEntries + i) * 2;
-    S += p[0];
-    N += p[1];
+  if (i < nc) {
+#pragma unroll 16
+    for (int g = j; g < G; g += 16) {
+      const long long* p = part + (((size_t)m * kQzGroups + g) * kQzMaxEntries + i) * 2;
+      S += p[0];
+      N += p[1];
+    }
   }
-  if (N > 0) {
-    const long long num = 2 * S + N, den = 2 * N;
-    long long q = num / den;                       // truncates toward zero
-    if (num % den != 0 && num < 0) q -= 1;          // floor
-    c[(size_t)m * kQzMaxEntries + i] = q;
+  sS[i][j] = S;
+  sN[i][j] = N;
+  __syncthreads();
+  if (j == 0 && i < nc) {
+    S = 0;
+    N = 0;
+    for (int r = 0; r < 16; ++r) {
+      S += sS[i][r];
+      N += sN[i][r];
+    }
+    if (N > 0) {
+      const long long num = 2 * S + N, den = 2 * N;
+      long long q = num / den;                       // truncates toward zero
+      if (num % den != 0 && num < 0) q -= 1;          // floor
+      c[(size_t)m * kQzMaxEntries + i] = q;
+    }
   }
 }
 
@@ -277,8 +335,8 @@ int launch_quantize(int32_t n, int64_t rows, int64_t k, const float* w, int32_t 
                     const QzWs& ws, hipStream_t s) {
   constexpr int NC = 1 << FMT;
   const size_t nw = (size_t)n * rows * k, nb_total = nw / 32;
-  launch_kernel("qz_norm", k_qz_norm<FMT>, dim3((unsigned)((nw + 255) / 256)), dim3(256), s, w, nw, n, ws.v, ws.sc,
-                ws.c);
+  launch_kernel("qz_norm", k_qz_norm<FMT>, dim3((unsigned)((nw / 4 + 255) / 256)), dim3(256), s, w, nw, n, ws.v,
+                ws.sc, ws.c);
   if (n * kQzMaxEntries > 256)
     launch_kernel("qz_init", k_qz_init, dim3((unsigned)((n * kQzMaxEntries + 255) / 256)), dim3(256), s, ws.c, n, NC);
   int st = launch_check("qz_norm");
@@ -287,7 +345,7 @@ int launch_quantize(int32_t n, int64_t rows, int64_t k, const float* w, int32_t 
   for (int it = 0; it < iters; ++it) {
     launch_kernel("qz_assign", k_qz_assign<NC>, dim3(kQzGroups, n), dim3(256), s, (const int16_t*)ws.v, per_mat,
                   (const long long*)ws.c, ws.part);
-    launch_kernel("qz_update", k_qz_update, dim3(n), dim3(64), s, ws.c, (const long long*)ws.part, kQzGroups, NC);
+    launch_kernel("qz_update", k_qz_update, dim3(n), dim3(256), s, ws.c, (const long long*)ws.part, kQzGroups, NC);
     if ((st = launch_check("qz_lloyd"))) return st;
   }
   const size_t row_bytes = (size_t)(k / 32) * (FMT == 2 ? 10 : FMT == 3 ? 14 : 17);

@@ -78,3 +78,33 @@ def test_quantize_repeat_identical():
     run(2, gen.float_matrices(2, 64, 512, seed=61), 5, ws)   # stale workspace contents in between
     b = run(2, w, 5, ws)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("fmt,k", [(2, 256), (3, 256), (4, 512)])
+def test_quantize_midpoint_ties(fmt, k):
+    """Normalized values exactly on the midpoints between starting centroids
+    (ties, which go to the lower entry) and on the centroids themselves; the
+    first assignment pass decides every tie, so a wrong tie rule changes the
+    fitted codebook and the codes."""
+    nc = 1 << formats.BITS[fmt]
+    step = 254.0 / nc                                   # cell width in units of d
+    mids = [-127.0 + step * i for i in range(1, nc)]    # midpoints between starts
+    cents = [-127.0 + step * (i + 0.5) for i in range(nc)]
+    vals = np.array(mids + cents, dtype=np.float64)
+    rows = 4
+    rng = np.random.default_rng(70 + fmt)
+    if fmt == 4:
+        d = np.ldexp(1.0, rng.integers(-10, -3, size=(rows, k // 32)))
+    else:
+        d = rng.uniform(0.01, 0.1, size=(rows, k // 32)).astype(np.float16).astype(np.float64)
+    idx = rng.integers(0, len(vals), size=(rows, k))
+    u = vals[idx].reshape(rows, k // 32, 32)
+    u[:, :, 0] = np.where(rng.integers(0, 2, size=(rows, k // 32)) == 1, 127.0, -127.0)
+    w = (u * d[..., None]).reshape(1, rows, k)
+    assert np.array_equal(w.astype(np.float32).astype(np.float64), w)   # exact in fp32
+    w = w.astype(np.float32)
+    for iters in (1, 3):
+        packed, cb = run(fmt, w, iters)
+        ref_packed, ref_cb, _, _ = quantize.quantize(fmt, w, iters)
+        assert np.array_equal(cb, ref_cb)
+        assert np.array_equal(packed, ref_packed)
