@@ -54,6 +54,7 @@ def parse():
                     help="before the benchmark, copy MIB MiB device-to-device once (a plain copy of known size, "
                          "for scaling memory-traffic counters)")
     ap.add_argument("--prefill-only", action="store_true", help="only the 8K-token prefill (for profiling)")
+    ap.add_argument("--quantize-only", action="store_true", help="only the weight quantizer (for profiling)")
     return ap.parse_args()
 
 
@@ -117,6 +118,9 @@ def main():
     if args.prefill_only:
         res = bench_prefill(torch, qm, gen, spec, dl, dev)
         print(json.dumps({"prefill_8k": res}), flush=True)
+        return
+    if args.quantize_only:
+        print(json.dumps({"quantize_fp2": bench_quantize(torch, qm, gen, dev)}), flush=True)
         return
     ws = dl.workspace(4)
     toks = torch.from_numpy(gen.tokens(64, spec.hidden, seed=0, stream=7)).to(dev)
