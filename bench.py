@@ -141,6 +141,31 @@ def main():
     value = bytes_q1 / (ms * 1e-3) / 1e9
     log(f"decode q=1: {ms * 1e3:.2f} us/call, {value:.1f} GB/s effective")
 
+    # the same calls captured once as a HIP graph (64 calls, one per rotating
+    # token) and replayed: the steady state of a decode loop that replays its
+    # layer launches
+    g_stream = torch.cuda.Stream()
+    g_stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(g_stream):
+        for i in range(64):
+            decode_q1(i)
+    torch.cuda.current_stream().wait_stream(g_stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(64):
+            decode_q1(i)
+    for _ in range(2):
+        graph.replay()
+    reps = max(1, K // 64)
+    with Timer(torch) as tg:
+        for _ in range(reps):
+            graph.replay()
+    ms_graph = tg.ms / (reps * 64)
+    log(f"decode q=1 graph replay: {ms_graph * 1e3:.2f} us/call, "
+        f"{bytes_q1 / (ms_graph * 1e-3) / 1e9:.1f} GB/s effective")
+    del graph
+
     # dominant kernel, timed with HIP events on the launch stream over K calls
     qm.qmoe_timing_enable(True)
     for i in range(K):
@@ -162,7 +187,9 @@ def main():
     extra = {"decode_q1": {"us_per_call": round(ms * 1e3, 2), "tokens_per_s": round(1.0 / (ms * 1e-3), 1),
                            "effective_GBps": round(value, 1), "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
                            "kernel_us": {k: round(v * 1e3, 2) for k, v in kern.items() if v},
-                           "down_kernel_GBps": round(down_gbs, 1)}}
+                           "down_kernel_GBps": round(down_gbs, 1),
+                           "graph_replay_us_per_call": round(ms_graph * 1e3, 2),
+                           "graph_replay_GBps": round(bytes_q1 / (ms_graph * 1e-3) / 1e9, 1)}}
 
     if not args.no_extra:
         extra.update(bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev))
@@ -284,6 +311,29 @@ def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
         res[f"dense_mix_q{ncols}"] = {"us_per_step": round(ms * 1e3, 2), "effective_GBps": round(gbs, 1),
                                       "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "packed_bytes": nbytes}
         log(f"dense mix q={ncols}: {ms * 1e3:.2f} us, {gbs:.1f} GB/s")
+
+    # ---------------------------------------------------------------- fused versus expand-then-multiply
+    fp3_big = gen.matvec_case(3, 4096, 16384, ncols=1, seed=0, rot=1)
+    for name, fmt_x, c in (("fp3_4096x2048_h32", 3, fp3), ("fp3_4096x16384_h32", 3, fp3_big),
+                           ("fp4_4096x16384", 4, fp4)):
+        m = qm.device.DeviceMatrix(c)
+        x1 = torch.from_numpy(c.x[:1]).to(dev)
+        y1 = torch.empty((1, c.rows), dtype=torch.float32, device=dev)
+        ws_f = m.workspace(1)
+        ws_x = torch.empty(qm.qmoe_matvec_expanded_workspace_bytes(c.rows, c.k, 1), dtype=torch.uint8, device=dev)
+        t_ = {}
+        for label, fn, w_ in (("fused", qm.qmoe_matvec, ws_f), ("expand_then_multiply", qm.qmoe_matvec_expanded, ws_x)):
+            for _ in range(10):
+                fn(fmt_x, c.rows, c.k, m.w, m.cb, c.rot, x1, y1, w_)
+            with Timer(torch) as tm:
+                for _ in range(K):
+                    fn(fmt_x, c.rows, c.k, m.w, m.cb, c.rot, x1, y1, w_)
+            t_[label] = tm.ms / K * 1e3
+        res[f"matvec_fusion_{name}"] = {"fused_us": round(t_["fused"], 2),
+                                         "expand_then_multiply_us": round(t_["expand_then_multiply"], 2),
+                                         "fused_speedup": round(t_["expand_then_multiply"] / t_["fused"], 2)}
+        log(f"matvec {name} q=1: fused {t_['fused']:.2f} us, expand-then-multiply "
+            f"{t_['expand_then_multiply']:.2f} us ({t_['expand_then_multiply'] / t_['fused']:.2f}x)")
 
     # ---------------------------------------------------------------- weight quantizer
     res["quantize_fp2"] = bench_quantize(torch, qm, gen, dev)

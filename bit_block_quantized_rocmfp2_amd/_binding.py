@@ -78,6 +78,9 @@ def _load():
         "qmoe_matvec_workspace_bytes": (c_size_t, [c_int64, c_int32]),
         "qmoe_matvec": (c_int, [c_int, c_int64, c_int64, c_void_p, c_size_t, c_void_p, c_int32, c_void_p, c_int32,
                                 c_void_p, c_void_p, c_size_t, c_void_p]),
+        "qmoe_matvec_expanded_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int32]),
+        "qmoe_matvec_expanded": (c_int, [c_int, c_int64, c_int64, c_void_p, c_size_t, c_void_p, c_int32, c_void_p,
+                                         c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
         "qmoe_quant_act": (c_int, [c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
         "qmoe_block_dots": (c_int, [c_int, c_int64, c_int64, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p,
                                     c_void_p]),
@@ -100,7 +103,7 @@ EXPORTED = (
     "qmoe_strerror", "qmoe_last_error", "qmoe_version", "qmoe_block_bytes", "qmoe_packed_bytes", "qmoe_pack",
     "qmoe_unpack", "qmoe_layer_check", "qmoe_workspace_bytes", "qmoe_workspace_layout", "qmoe_route",
     "qmoe_decode_layer", "qmoe_prefill_layer", "qmoe_matvec_workspace_bytes", "qmoe_matvec", "qmoe_quant_act",
-    "qmoe_block_dots", "qmoe_quantize_workspace_bytes", "qmoe_quantize", "qmoe_timing_enable", "qmoe_timing_read",
+    "qmoe_block_dots", "qmoe_matvec_expanded_workspace_bytes", "qmoe_matvec_expanded", "qmoe_quantize_workspace_bytes", "qmoe_quantize", "qmoe_timing_enable", "qmoe_timing_read",
 )
 
 
@@ -220,6 +223,15 @@ def qmoe_prefill_layer(L, x, out, ws, stream=None) -> None:
 def qmoe_matvec(fmt, rows, k, w, cb, rot, x, y, ws, stream=None) -> None:
     _check(LIB.qmoe_matvec(fmt, rows, k, _ptr(w), _nbytes(w), _ptr(cb), rot, _ptr(x), x.shape[0], _ptr(y),
                            _ptr(ws), _nbytes(ws), _stream(stream)), "qmoe_matvec")
+
+
+def qmoe_matvec_expanded_workspace_bytes(rows: int, k: int, ncols: int) -> int:
+    return LIB.qmoe_matvec_expanded_workspace_bytes(rows, k, ncols)
+
+
+def qmoe_matvec_expanded(fmt, rows, k, w, cb, rot, x, y, ws, stream=None) -> None:
+    _check(LIB.qmoe_matvec_expanded(fmt, rows, k, _ptr(w), _nbytes(w), _ptr(cb), rot, _ptr(x), x.shape[0], _ptr(y),
+                                    _ptr(ws), _nbytes(ws), _stream(stream)), "qmoe_matvec_expanded")
 
 
 def qmoe_quant_act(x, rot, xq, dx, stream=None) -> None:

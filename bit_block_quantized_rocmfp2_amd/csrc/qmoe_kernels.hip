@@ -253,6 +253,82 @@ __global__ __launch_bounds__(256) void k_matvec(const uint8_t* __restrict__ W, i
   }
 }
 
+// ------------------------------------------------------------ expand-then-multiply (comparison path)
+// The unfused form of k_matvec, kept to measure what fusion saves ([0731-Strix]
+// section "Lucebox Engine integration with Geometric": the fused 3.5-bit
+// matvec against the expand-then-multiply fallback). k_expand writes every
+// block as 32 int8 weights C[code] and an fp32 scale; k_matvec_x multiplies the
+// expanded matrix with k_matvec's lane mapping and accumulation order, so the
+// outputs are identical bit for bit and only the bytes moved differ
+// (1 + 1/8 B per weight read, plus the expansion's own pass, against 0.31 to
+// 0.53 B).
+template <int FMT>
+__global__ __launch_bounds__(256) void k_expand(const uint8_t* __restrict__ W, int64_t rows, size_t row_bytes, int nb,
+                                                const int8_t* __restrict__ cbp, int8_t* __restrict__ w8,
+                                                float* __restrict__ s32) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * nb) return;
+  const int64_t r = i / nb;
+  const int b = (int)(i % nb);
+  uint32_t cb[4];
+  load_codebook<FMT>(cbp, cb);
+  Blocks<FMT, 1> bl;
+  bl.load(W + (size_t)r * row_bytes, nb, b);
+  uint32_t w[8];
+  bl.expand(0, cb, w);
+  u32x4* dst = reinterpret_cast<u32x4*>(w8 + (size_t)i * 32);
+  dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+  dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+  s32[i] = bl.scale(0);
+}
+
+template <int NBL, int Q>
+__global__ __launch_bounds__(256) void k_matvec_x(const int8_t* __restrict__ w8, const float* __restrict__ s32,
+                                                  int64_t rows, int nb, int lpr_log2, const int8_t* __restrict__ xq,
+                                                  const float* __restrict__ dx, float* __restrict__ y) {
+  const int lpr = 1 << lpr_log2;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sub = lane >> lpr_log2, sl = lane & (lpr - 1);
+  const int rows_per_wave = 64 >> lpr_log2;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + wave) * rows_per_wave + sub;
+  const bool row_ok = row < rows;
+  float acc[Q];
+#pragma unroll
+  for (int t = 0; t < Q; ++t) acc[t] = 0.0f;
+  const int8_t* roww = w8 + (size_t)row * nb * 32;
+  const float* rows32 = s32 + (size_t)row * nb;
+  for (int c0 = 0; c0 < nb; c0 += lpr * NBL) {
+    const int b = c0 + sl * NBL;
+    if (row_ok && b < nb) {
+      uint32_t w[NBL][8];
+      float sc[NBL];
+#pragma unroll
+      for (int i = 0; i < NBL; ++i) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(roww + (size_t)(b + i) * 32);
+        const u32x4 a = p[0], c = p[1];
+        w[i][0] = a.x; w[i][1] = a.y; w[i][2] = a.z; w[i][3] = a.w;
+        w[i][4] = c.x; w[i][5] = c.y; w[i][6] = c.z; w[i][7] = c.w;
+        sc[i] = rows32[b + i];
+      }
+      Acts<NBL> act[Q];
+#pragma unroll
+      for (int t = 0; t < Q; ++t) act[t].load(xq + (size_t)t * nb * 32, dx + (size_t)t * nb, b);
+#pragma unroll
+      for (int i = 0; i < NBL; ++i)
+#pragma unroll
+        for (int t = 0; t < Q; ++t) {
+          const int p = block_dot(w[i], act[t].q[i]);
+          acc[t] = fmaf((float)p, sc[i] * act[t].d[i], acc[t]);
+        }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < Q; ++t) {
+    const float v = group_sum(acc[t], lpr);
+    if (sl == 0 && row_ok) y[(size_t)t * rows + row] = v;
+  }
+}
+
 // ------------------------------------------------------------ per-block integer sums (test entry)
 template <int FMT>
 __global__ __launch_bounds__(256) void k_block_dots(const uint8_t* __restrict__ W, int64_t rows, size_t row_bytes,
@@ -487,6 +563,68 @@ extern "C" int qmoe_matvec(int fmt, int64_t rows, int64_t k, const void* w, size
     default: launch_matvec_f<4>(ncols, W, rows, row_bytes, nb, lg, cb, xq, dx, y, s); break;
   }
   return launch_check("matvec");
+}
+
+extern "C" size_t qmoe_matvec_expanded_workspace_bytes(int64_t rows, int64_t k, int32_t ncols) {
+  const size_t base = qmoe_matvec_workspace_bytes(k, ncols);
+  if (!base || rows < 0) return 0;
+  return base + round_up((size_t)rows * k, 256) + round_up((size_t)rows * (k / 32) * 4, 256);
+}
+
+template <int NBL>
+void launch_matvec_x(int q, const int8_t* w8, const float* s32, int64_t rows, int nb, int lg, const int8_t* xq,
+                     const float* dx, float* y, hipStream_t s) {
+  const int rows_per_wg = 4 * (64 >> lg);
+  const dim3 grid((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
+  switch (q) {
+    case 1: launch_kernel("matvec_x", k_matvec_x<NBL, 1>, grid, dim3(256), s, w8, s32, rows, nb, lg, xq, dx, y); break;
+    case 2: launch_kernel("matvec_x", k_matvec_x<NBL, 2>, grid, dim3(256), s, w8, s32, rows, nb, lg, xq, dx, y); break;
+    case 3: launch_kernel("matvec_x", k_matvec_x<NBL, 3>, grid, dim3(256), s, w8, s32, rows, nb, lg, xq, dx, y); break;
+    default: launch_kernel("matvec_x", k_matvec_x<NBL, 4>, grid, dim3(256), s, w8, s32, rows, nb, lg, xq, dx, y);
+  }
+}
+
+extern "C" int qmoe_matvec_expanded(int fmt, int64_t rows, int64_t k, const void* w, size_t w_bytes, const int8_t* cb,
+                                    int32_t rot, const float* x, int32_t ncols, float* y, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  clear_error();
+  FormatInfo fi;
+  int st = check_matrix(fmt, rows, k, w, w_bytes, cb, &fi);
+  if (st) return st;
+  if (rot != 0 && rot != 1) QMOE_FAIL(QMOE_E_FORMAT, "rot=%d unsupported (0 or 1)", rot);
+  if (ncols < 1 || ncols > 4) QMOE_FAIL(QMOE_E_SHAPE, "ncols=%d outside 1..4", ncols);
+  if (!x || !y) QMOE_FAIL(QMOE_E_INVAL, "NULL pointer");
+  if (!aligned16(x)) QMOE_FAIL(QMOE_E_INVAL, "x not 16-byte aligned");
+  const size_t need = qmoe_matvec_expanded_workspace_bytes(rows, k, ncols);
+  if (!ws) QMOE_FAIL(QMOE_E_WORKSPACE, "missing workspace (NULL)");
+  if (!aligned16(ws)) QMOE_FAIL(QMOE_E_WORKSPACE, "workspace not 16-byte aligned");
+  if (ws_bytes < need) QMOE_FAIL(QMOE_E_WORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  if (rows == 0) return QMOE_OK;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  int8_t* xq = reinterpret_cast<int8_t*>(base);
+  float* dx = reinterpret_cast<float*>(base + round_up((size_t)ncols * k, 256));
+  const size_t mv = qmoe_matvec_workspace_bytes(k, ncols);
+  int8_t* w8 = reinterpret_cast<int8_t*>(base + mv);
+  float* s32 = reinterpret_cast<float*>(base + mv + round_up((size_t)rows * k, 256));
+  hipStream_t s = as_stream(stream);
+  const int nb = (int)(k / 32);
+  if ((st = launch_quant(x, (int64_t)ncols * nb, rot, xq, dx, s))) return st;
+  const size_t row_bytes = (size_t)nb * fi.block_bytes;
+  const uint8_t* W = static_cast<const uint8_t*>(w);
+  const unsigned eg = (unsigned)((rows * nb + 255) / 256);
+  switch (fmt) {
+    case 2: launch_kernel("expand", k_expand<2>, dim3(eg), dim3(256), s, W, rows, row_bytes, nb, cb, w8, s32); break;
+    case 3: launch_kernel("expand", k_expand<3>, dim3(eg), dim3(256), s, W, rows, row_bytes, nb, cb, w8, s32); break;
+    default: launch_kernel("expand", k_expand<4>, dim3(eg), dim3(256), s, W, rows, row_bytes, nb, cb, w8, s32); break;
+  }
+  if ((st = launch_check("expand"))) return st;
+  const int nbl = fmt == 4 ? 1 : 2;
+  const int lg = ilog2(lanes_per_row(nb, nbl));
+  if (nbl == 2)
+    launch_matvec_x<2>(ncols, w8, s32, rows, nb, lg, xq, dx, y, s);
+  else
+    launch_matvec_x<1>(ncols, w8, s32, rows, nb, lg, xq, dx, y, s);
+  return launch_check("matvec_x");
 }
 
 extern "C" int qmoe_route(const qmoe_layer* L, const float* x, int32_t ntok, int32_t* idx, float* gate_w, void* ws,

@@ -144,6 +144,20 @@ int qmoe_decode_layer(const qmoe_layer* L, const float* x, int32_t q, float* out
 int qmoe_prefill_layer(const qmoe_layer* L, const float* x, int32_t ntok, float* out,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* Expand-then-multiply form of qmoe_matvec, the comparison path for the fused
+ * kernel ([0731-Strix], section "Lucebox Engine integration with Geometric":
+ * the fused 3.5-bit matrix-vector kernel against the generic expand-then-
+ * multiply fallback). It first writes every block of w as 32 int8 weights and
+ * an fp32 scale into the workspace, then multiplies the expanded matrix with
+ * the same lane mapping and accumulation order as qmoe_matvec, so y equals
+ * qmoe_matvec's output bit for bit. Arguments and errors as qmoe_matvec; ws:
+ * qmoe_matvec_expanded_workspace_bytes(rows, k, ncols) bytes, 16-byte aligned,
+ * caller-owned, scratch after the call. */
+size_t qmoe_matvec_expanded_workspace_bytes(int64_t rows, int64_t k, int32_t ncols);
+int qmoe_matvec_expanded(int fmt, int64_t rows, int64_t k, const void* w, size_t w_bytes,
+                         const int8_t* cb, int32_t rot, const float* x, int32_t ncols, float* y,
+                         void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes of qmoe_matvec for K = k and ncols columns. */
 size_t qmoe_matvec_workspace_bytes(int64_t k, int32_t ncols);
 
@@ -215,7 +229,7 @@ int qmoe_quantize(qmoe_format f, int32_t n, int64_t rows, int64_t k, const float
  * execution); (0) stops; either call discards earlier records.
  * qmoe_timing_read waits for the recorded kernels named `name` and returns
  * their summed time in ms and their count. Names: "quant_act", "router",
- * "topk", "matvec" (shared); "route", "gateup", "down" (decode);
+ * "topk", "matvec", "expand", "matvec_x" (shared); "route", "gateup", "down" (decode);
  * "group_count", "group_scan", "group_scatter", "gateup_mfma", "down_mfma",
  * "combine" (prefill); "qz_norm", "qz_assign", "qz_update", "qz_pack"
  * (quantizer). */

@@ -97,6 +97,31 @@ def test_matvec(fmt, rows, k, rot, ncols):
     assert np.array_equal(xq, xq_ref)
 
 
+@pytest.mark.parametrize("fmt,rows,k,rot", [(2, 300, 768, 1), (3, 129, 2048, 1), (3, 4096, 2048, 1),
+                                            (4, 70, 16384, 1)])
+@pytest.mark.parametrize("ncols", [1, 4])
+def test_matvec_expanded(fmt, rows, k, rot, ncols):
+    """The expand-then-multiply comparison path: the same outputs as the fused
+    matvec bit for bit (same lane mapping and accumulation order), hence the
+    oracle's within the tolerance; its workspace holds the expanded weights,
+    which equal codebook[code] of the oracle's unpacked codes."""
+    c = gen.matvec_case(fmt, rows, k, ncols=ncols, seed=31, rot=rot)
+    y_ref, _, _ = dots.matvec(fmt, c.codes, c.scales, c.cb, c.x, rot)
+    m = qm.device.DeviceMatrix(c)
+    x = dev(c.x)
+    y = torch.empty((ncols, rows), dtype=torch.float32, device="cuda")
+    ye = torch.empty_like(y)
+    qm.qmoe_matvec(fmt, rows, k, m.w, m.cb, rot, x, y, m.workspace(ncols))
+    wse = torch.empty(qm.qmoe_matvec_expanded_workspace_bytes(rows, k, ncols), dtype=torch.uint8, device="cuda")
+    qm.qmoe_matvec_expanded(fmt, rows, k, m.w, m.cb, rot, x, ye, wse)
+    torch.cuda.synchronize()
+    assert np.array_equal(ye.cpu().numpy().view(np.uint32), y.cpu().numpy().view(np.uint32))
+    assert moe.rel_l2(ye.cpu().numpy(), y_ref) < TOL
+    off = qm.qmoe_matvec_workspace_bytes(k, ncols)
+    w8 = wse[off: off + rows * k].cpu().numpy().view(np.int8).reshape(rows, k)
+    assert np.array_equal(w8, np.asarray(c.cb, dtype=np.int8)[c.codes.astype(np.int64)])
+
+
 def test_fp2_matvec_512x256():
     """FP2 512x256, one 4-entry codebook, batch 1, seed 0."""
     c = gen.fp2_matvec(0)
