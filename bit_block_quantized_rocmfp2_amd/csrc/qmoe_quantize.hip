@@ -376,6 +376,7 @@ extern "C" int qmoe_quantize(qmoe_format f, int32_t n, int64_t rows, int64_t k, 
               f == QMOE_FP4 ? 512 : 256);
   const size_t nw = (size_t)n * rows * k;
   if (nw > ((size_t)1 << 34)) QMOE_FAIL(QMOE_E_SHAPE, "quantize: %zu weights exceed 2^34", nw);
+  if (n > 65535) QMOE_FAIL(QMOE_E_SHAPE, "quantize: n=%d matrices exceed 65535 (one grid row each)", n);
   if (iters < 0 || iters > kQzMaxIters) QMOE_FAIL(QMOE_E_SHAPE, "quantize: iters=%d outside 0..%d", iters, kQzMaxIters);
   if (!w || !out || !cb || !ws) QMOE_FAIL(QMOE_E_INVAL, "quantize: NULL pointer");
   if (!aligned16(w) || !aligned16(out)) QMOE_FAIL(QMOE_E_INVAL, "quantize: w and out must be 16-byte aligned");

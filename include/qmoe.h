@@ -211,7 +211,8 @@ int qmoe_workspace_layout(const qmoe_layer* L, int32_t max_tokens, qmoe_ws_layou
  * scale/256, `iters` (0..64) Lloyd iterations of a 1-D k-means per matrix in
  * integer arithmetic (results independent of reduction order), then the
  * nearest codebook entry of each weight (ties to the lower entry).
- * k: a multiple of 256 (FP2/FP3) or 512 (FP4). ws: caller-owned device
+ * k: a multiple of 256 (FP2/FP3) or 512 (FP4); n <= 65535; n*rows*k <= 2^34.
+ * ws: caller-owned device
  * workspace of qmoe_quantize_workspace_bytes(n, rows, k) bytes, 256-byte
  * aligned; its contents need no initialisation and are scratch afterwards.
  * Asynchronous on `stream`; never allocates or synchronises. Errors (checked

@@ -231,5 +231,6 @@ def test_quantize_rejects_bad_arguments_before_launch():
     assert call(ob=10) == -8                               # out too small
     assert call(wsb=100) == -6                             # workspace too small
     assert call(fmt=4, k=256) == -2                        # FP4 needs k % 512 == 0
+    assert call(n=70000, rows=1) == -2                     # more matrices than grid rows
     assert qm.qmoe_quantize_workspace_bytes(1, 4, 33) == 0
     assert qm.qmoe_quantize_workspace_bytes(2, 2048, 4096) >= 2 * 2048 * 4096 * 2
