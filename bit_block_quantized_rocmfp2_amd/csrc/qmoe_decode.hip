@@ -562,10 +562,13 @@ __global__ __launch_bounds__(256) void k_down(DecodeArgs a) {
 
 // Two to four tokens, when one pass covers the blocks and the routed
 // (expert, token) slots' activations fit 48 KB: the workgroup lists the slots of
-// the plan, copies their activations to LDS with direct 16-byte global -> LDS
-// loads (no registers), and requests the weight blocks of up to 12 experts in
-// the same round trip; each block is expanded once and applied to every routed
-// column. k_down instead loads each lane's own copy of every slot's activations
+// the plan, requests their activations (16-byte pieces into registers, copied to
+// LDS) and then the weight blocks of up to 12 experts, all in one round trip;
+// each expert's products wait only for that expert's blocks, so the arithmetic
+// of the first experts overlaps the arrival of the rest. (Direct global -> LDS
+// loads of the activations save registers, but the compiler does not track
+// them, so the kernel had to wait for every load before the first product.)
+// Each block is expanded once and applied to every routed column. k_down instead loads each lane's own copy of every slot's activations
 // after that expert's weights. The per-lane accumulation order is that of k_down
 // (experts ascending, then columns, then the lane's blocks).
 constexpr int kDownqActPieces = 48 * 1024 / 16;   // 16-byte pieces of staged activations
@@ -575,7 +578,6 @@ __global__ __launch_bounds__(256) void k_downq(DecodeArgs a) {
   constexpr int NBL = (FMT == 4) ? 1 : 2;
   constexpr int UB = 12;
   constexpr int CPL = 2 * NBL;   // 16-byte activation pieces per lane and slot
-  typedef __attribute__((address_space(3))) void lds_void;
   const int lpr_log2 = a.dn_lpr_log2;
   const int lpr = 1 << lpr_log2;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -618,7 +620,33 @@ __global__ __launch_bounds__(256) void k_downq(DecodeArgs a) {
   const int b = sl * NBL;
   const bool ok = row < a.hidden && b < nb;
   const int rowc = min(row, a.hidden - 1), bc = min(b, nb - NBL);
-  // weights of the first group of experts (unconditional, clamped loads)
+  // activations of the listed slots, requested first into registers (so that
+  // the compiler's waits before the LDS stores cover these loads only): LDS
+  // piece (within slot c) m * lpr + l holds piece l * CPL + m of the slot's
+  // row, so that each read of the lanes of one row touches consecutive pieces.
+  // Every load is issued (index clamped); only the stores are restricted.
+  const int pps = nb * 2;   // pieces per slot (= lpr * CPL)
+  const int nq = nslot * pps;
+  const int nd = nslot * (nb / 4);   // 16-byte pieces of scales (4 per piece)
+  constexpr int AP = kDownqActPieces / 256;
+  constexpr int DP = (kDownqMaxSlots * 16 + 255) / 256;
+  u32x4 av[AP], dv[DP];
+#pragma unroll
+  for (int k = 0; k < AP; ++k) {
+    const int P = min(tid + 256 * k, nq - 1);
+    const int c = P / pps, within = P % pps;
+    const int g = (within % lpr) * CPL + within / lpr;
+    av[k] = *reinterpret_cast<const u32x4*>(a.hq + (size_t)s_slot[c] * a.inter + (size_t)g * 16);
+  }
+#pragma unroll
+  for (int k = 0; k < DP; ++k) {
+    const int P = min(tid + 256 * k, nd - 1);
+    const int c = P / (nb / 4), within = P % (nb / 4);
+    dv[k] = *reinterpret_cast<const u32x4*>(a.dh + (size_t)s_slot[c] * nb + (size_t)within * 4);
+  }
+  // weights of the first group of experts (unconditional, clamped loads), all
+  // requested before any is used; each expert's products below wait for its
+  // own blocks only, so the arithmetic overlaps the rest of the stream
   int ej[UB];
   uint32_t cb[UB][4];
   Blocks<FMT, NBL> bl[UB];
@@ -628,26 +656,13 @@ __global__ __launch_bounds__(256) void k_downq(DecodeArgs a) {
     load_codebook<FMT>(a.cb_down + ((size_t)ej[j] << FMT), cb[j]);
     bl[j].load(a.down + (size_t)ej[j] * a.dn_stride + (size_t)rowc * a.dn_row_bytes, nb, bc);
   }
-  // activations of the listed slots: LDS piece (within slot c) m * lpr + l holds
-  // piece l * CPL + m of the slot's row, so that each read of the lanes of one
-  // row touches consecutive pieces; pieces past the end repeat the last slot
-  const int pps = nb * 2;   // pieces per slot (= lpr * CPL)
-  const int nq = nslot * pps;
-  for (int r0 = 0; r0 < nq; r0 += 256) {
-    const int P = r0 + 64 * wave + lane;
-    const int c = min(P / pps, nslot - 1), within = P % pps;
-    const int g = (within % lpr) * CPL + within / lpr;
-    const int8_t* src = a.hq + (size_t)s_slot[c] * a.inter + (size_t)g * 16;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(s_act + r0 + 64 * wave), 16, 0, 0);
-  }
-  const int nd = nslot * (nb / 4);   // 16-byte pieces of scales (4 per piece)
-  for (int r0 = 0; r0 < nd; r0 += 256) {
-    const int P = r0 + 64 * wave + lane;
-    const int c = min(P / (nb / 4), nslot - 1), within = P % (nb / 4);
-    const float* src = a.dh + (size_t)s_slot[c] * nb + (size_t)within * 4;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(s_dh + r0 + 64 * wave), 16, 0, 0);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < AP; ++k)
+    if (tid + 256 * k < nq) s_act[tid + 256 * k] = av[k];
+#pragma unroll
+  for (int k = 0; k < DP; ++k)
+    if (tid + 256 * k < nd) s_dh[tid + 256 * k] = dv[k];
   __syncthreads();
   const float* dh = reinterpret_cast<const float*>(s_dh);
   float acc[Q];
