@@ -141,6 +141,36 @@ def main():
     value = bytes_q1 / (ms * 1e-3) / 1e9
     log(f"decode q=1: {ms * 1e3:.2f} us/call, {value:.1f} GB/s effective")
 
+    # cold-cache variant: before each call a 512 MiB device write (not timed)
+    # evicts the 256 MB last-level cache and the L2s, then the call alone is
+    # timed with events on the stream
+    # (the same single-call timing after a 4 KiB write separates the cost of
+    # timing a call alone from the cost of the cold cache)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(64)]
+
+    def single_calls(nbytes, read_only=False):
+        buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+        acc = torch.zeros(1, dtype=torch.int32, device=dev)
+        t_ = []
+        for rep in range(2):
+            for i in range(64):
+                if read_only:
+                    torch.amax(buf, dim=0, keepdim=True, out=acc)   # reads the buffer, writes 4 bytes
+                else:
+                    buf.fill_(rep + i)
+                ev[i][0].record()
+                decode_q1(i)
+                ev[i][1].record()
+            torch.cuda.synchronize()
+            t_ += [a.elapsed_time(b) for a, b in ev]
+        del buf
+        return float(np.mean(t_[64:]))
+    ms_cold = single_calls(512 << 20)
+    ms_cold_r = single_calls(512 << 20, read_only=True)
+    ms_single = single_calls(4096)
+    log(f"decode q=1 single calls: {ms_cold * 1e3:.2f} us after a 512 MiB write, {ms_cold_r * 1e3:.2f} us after a "
+        f"512 MiB read, {ms_single * 1e3:.2f} us after a 4 KiB write (mean of 64)")
+
     # the same calls captured once as a HIP graph (64 calls, one per rotating
     # token) and replayed: the steady state of a decode loop that replays its
     # layer launches
@@ -188,6 +218,9 @@ def main():
                            "effective_GBps": round(value, 1), "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
                            "kernel_us": {k: round(v * 1e3, 2) for k, v in kern.items() if v},
                            "down_kernel_GBps": round(down_gbs, 1),
+                           "single_call_after_512MiB_write_us": round(ms_cold * 1e3, 2),
+                           "single_call_after_512MiB_read_us": round(ms_cold_r * 1e3, 2),
+                           "single_call_warm_us": round(ms_single * 1e3, 2),
                            "graph_replay_us_per_call": round(ms_graph * 1e3, 2),
                            "graph_replay_GBps": round(bytes_q1 / (ms_graph * 1e-3) / 1e9, 1)}}
 
