@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits,
 
 // ------------------------------------------------------------ dense matvec (1..4 columns)
 // Each wave handles 64/LPR rows at once (LPR lanes per row, NBL blocks per lane).
-template <int FMT, int Q>
+template <int FMT, int Q, int UF>
 __global__ __launch_bounds__(256) void k_matvec(const uint8_t* __restrict__ W, int64_t rows, size_t row_bytes, int nb,
                                                 int lpr_log2, const int8_t* __restrict__ cbp,
                                                 const int8_t* __restrict__ xq, const float* __restrict__ dx,
@@ -224,24 +224,36 @@ __global__ __launch_bounds__(256) void k_matvec(const uint8_t* __restrict__ W, i
   float acc[Q];
 #pragma unroll
   for (int t = 0; t < Q; ++t) acc[t] = 0.0f;
-  const uint8_t* rowp = W + (size_t)row * row_bytes;
-  for (int c0 = 0; c0 < nb; c0 += lpr * NBL) {
-    const int b = c0 + sl * NBL;
-    if (row_ok && b < nb) {
-      Blocks<FMT, NBL> bl;
-      bl.load(rowp, nb, b);
-      Acts<NBL> act[Q];
+  // UF chunks of the row (lpr * NBL blocks each) per step: the loads of all UF
+  // chunks are issued (clamped into range) before any is used, so a wave makes
+  // one memory round trip per UF chunks; the products are taken chunk by chunk
+  // in ascending order, as a one-chunk loop would (UF = 1 when a row is one chunk)
+  const uint8_t* rowp = W + (size_t)(row_ok ? row : rows - 1) * row_bytes;
+  for (int c0 = 0; c0 < nb; c0 += UF * lpr * NBL) {
+    Blocks<FMT, NBL> bl[UF];
+    Acts<NBL> act[UF][Q];
 #pragma unroll
-      for (int t = 0; t < Q; ++t) act[t].load(xq + (size_t)t * nb * 32, dx + (size_t)t * nb, b);
+    for (int u = 0; u < UF; ++u) {
+      const int bc = min(c0 + u * lpr * NBL + sl * NBL, nb - NBL);
+      bl[u].load(rowp, nb, bc);
 #pragma unroll
-      for (int i = 0; i < NBL; ++i) {
-        uint32_t w[8];
-        bl.expand(i, cb, w);
-        const float s = bl.scale(i);
+      for (int t = 0; t < Q; ++t) act[u][t].load(xq + (size_t)t * nb * 32, dx + (size_t)t * nb, bc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < Q; ++t) {
-          const int p = block_dot(w, act[t].q[i]);
-          acc[t] = fmaf((float)p, s * act[t].d[i], acc[t]);
+    for (int u = 0; u < UF; ++u) {
+      const int b = c0 + u * lpr * NBL + sl * NBL;
+      if (row_ok && b < nb) {
+#pragma unroll
+        for (int i = 0; i < NBL; ++i) {
+          uint32_t w[8];
+          bl[u].expand(i, cb, w);
+          const float s = bl[u].scale(i);
+#pragma unroll
+          for (int t = 0; t < Q; ++t) {
+            const int p = block_dot(w, act[u][t].q[i]);
+            acc[t] = fmaf((float)p, s * act[u][t].d[i], acc[t]);
+          }
         }
       }
     }
@@ -463,7 +475,14 @@ void launch_matvec_t(const uint8_t* W, int64_t rows, size_t row_bytes, int nb, i
                      const int8_t* xq, const float* dx, float* y, hipStream_t s) {
   const int rows_per_wg = 4 * (64 >> lpr_log2);
   const unsigned grid = (unsigned)((rows + rows_per_wg - 1) / rows_per_wg);
-  launch_kernel("matvec", k_matvec<FMT, Q>, dim3(grid), dim3(256), s, W, rows, row_bytes, nb, lpr_log2, cb, xq, dx, y);
+  constexpr int NBL = (FMT == 4) ? 1 : 2;
+  const int chunks = (nb + (NBL << lpr_log2) - 1) / (NBL << lpr_log2);
+  if (chunks == 1)
+    launch_kernel("matvec", k_matvec<FMT, Q, 1>, dim3(grid), dim3(256), s, W, rows, row_bytes, nb, lpr_log2, cb, xq,
+                  dx, y);
+  else
+    launch_kernel("matvec", k_matvec<FMT, Q, (Q <= 2) ? 4 : 2>, dim3(grid), dim3(256), s, W, rows, row_bytes, nb,
+                  lpr_log2, cb, xq, dx, y);
 }
 
 template <int FMT>
