@@ -214,7 +214,25 @@ def main():
                 "kernel": "k_gateup1<2> (6 experts x gate+up FP2 = 31,457,280 algorithmic bytes per launch)"}
     down_gbs = spec.topk * down_bytes / (kern["down"] * 1e-3) / 1e9
 
+    # measured HBM stream reference (STREAM "copy" convention): a 1 GiB
+    # device-to-device copy, bytes read + bytes written over its time
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    with Timer(torch) as tr:
+        for _ in range(10):
+            dst.copy_(src)
+    read_gbs = 2 * (1 << 30) / (tr.ms / 10 * 1e-3) / 1e9
+    del src, dst
+    log(f"HBM stream reference (1 GiB device copy, read + write bytes): {read_gbs:.1f} GB/s")
+    router_bytes = spec.n_experts * spec.hidden * 2
+    roofline["measured_stream_peak"] = round(read_gbs, 1)
+    roofline["frac_of_measured_stream_peak"] = round(achieved / read_gbs, 4)
+
     extra = {"decode_q1": {"us_per_call": round(ms * 1e3, 2), "tokens_per_s": round(1.0 / (ms * 1e-3), 1),
+                           "effective_GBps_with_router": round((bytes_q1 + router_bytes) / (ms * 1e-3) / 1e9, 1),
+                           "frac_of_measured_stream_peak": round(value / read_gbs, 4),
                            "effective_GBps": round(value, 1), "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
                            "kernel_us": {k: round(v * 1e3, 2) for k, v in kern.items() if v},
                            "down_kernel_GBps": round(down_gbs, 1),
