@@ -315,18 +315,29 @@ __device__ __forceinline__ double router_block_sum(const uint16_t* __restrict__ 
                                                    int H, int e, int b, int nb) {
   if (b >= nb) return 0.0;
   const u32x4* wp = reinterpret_cast<const u32x4*>(W + (size_t)e * H + (size_t)b * 32);
+  const u32x4* xp = reinterpret_cast<const u32x4*>(x + (size_t)b * 32);
+  u32x4 wr[4], xr[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wr[i] = wp[i];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xr[i] = xp[i];
+  // the weights and all 32 activations arrive in one memory round trip before
+  // the first product: the empty statement takes every loaded piece as an
+  // input (left to itself the compiler sank the last pieces between the
+  // products of this dependent chain, a second round trip on the router's
+  // critical path)
+  asm volatile("" ::"v"(wr[0]), "v"(wr[1]), "v"(wr[2]), "v"(wr[3]), "v"(xr[0]), "v"(xr[1]), "v"(xr[2]),
+               "v"(xr[3]), "v"(xr[4]), "v"(xr[5]), "v"(xr[6]), "v"(xr[7]));
   uint32_t wv[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u32x4 u = wp[i];
-    wv[4 * i] = u.x; wv[4 * i + 1] = u.y; wv[4 * i + 2] = u.z; wv[4 * i + 3] = u.w;
+    wv[4 * i] = wr[i].x; wv[4 * i + 1] = wr[i].y; wv[4 * i + 2] = wr[i].z; wv[4 * i + 3] = wr[i].w;
   }
-  const float4* xp = reinterpret_cast<const float4*>(x + (size_t)b * 32);
   double acc = 0.0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float4 f = xp[i];
-    const float xs[4] = {f.x, f.y, f.z, f.w};
+    const float xs[4] = {__uint_as_float(xr[i].x), __uint_as_float(xr[i].y), __uint_as_float(xr[i].z),
+                         __uint_as_float(xr[i].w)};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int j = 4 * i + k;
@@ -477,10 +488,19 @@ __device__ __forceinline__ uint64_t topk_select_ns(const double* __restrict__ ro
                                                    TopkPick& p) {
   uint64_t key[NS];
   int id[NS];
+  // every slot's load is issued (index clamped) before any is used, and every
+  // key is formed before the bound is applied by a select: one memory round
+  // trip for the row (a load whose value is used only under e < E is sunk into
+  // that branch and waits there on its own)
+  double lg[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) lg[j] = row[min(lane + 64 * j, E - 1)];
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const int e = lane + 64 * j;
-    key[j] = (e < E) ? f64_order_key(row[e]) : 0;   // key 0: no candidate (no real logit maps to 0)
+    const uint64_t k = f64_order_key(lg[j]);
+    key[j] = (e < E) ? k : 0ull;   // key 0: no candidate (no real logit maps to 0)
     id[j] = e;
   }
   // sort the lane's slots into pick order (odd-even transposition: NS rounds)
