@@ -15,8 +15,9 @@
 //     fits on AMD Strix Halo" (gate/up 2.5 bpw, down 3.5 bpw, per-expert
 //     codebooks).
 //
-//   k_route    one workgroup per expert, one wave per token: fp64 logits; the
-//              workgroups also share the int8 quantization of the tokens.
+//   k_route    one workgroup per expert, two waves per token: fp64 logits;
+//              further workgroups of the same launch quantize the tokens to
+//              int8 blocks, alongside the logits.
 //   k_gateup   the gate/up launch. Every workgroup first selects the top-k of
 //              each token from the logits and builds the plan itself (the union
 //              of the chosen experts in ascending id, a column mask and the
@@ -93,6 +94,25 @@ __global__ __launch_bounds__(128 * Q) void k_route(DecodeArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t = w >> 1, h = w & 1;
   const int e = blockIdx.x;
+  if (e >= a.E) {
+    // workgroups past the experts quantize the tokens, quant_per_wg blocks
+    // each, two per wave pass (one per half-wave), alongside the logits rather
+    // than after them
+    const int nblk = a.q * a.nb_h, qi = e - a.E;
+    const int b_end = min((qi + 1) * a.quant_per_wg, nblk);
+    for (int b0 = qi * a.quant_per_wg + 2 * w; b0 < b_end; b0 += 4 * Q) {
+      const int b = b0 + (lane >> 5), j = lane & 31;
+      const bool ok = b < b_end;
+      const float v = ok ? a.x[(size_t)b * 32 + j] : 0.0f;
+      float d;
+      const uint32_t qw = quant_block32_lanes(v, a.rot_gateup, &d);
+      if (ok) {
+        if ((j & 3) == 0) reinterpret_cast<uint32_t*>(a.xq + (size_t)b * 32)[j >> 2] = qw;
+        if (j == 0) a.dx[b] = d;
+      }
+    }
+    return;
+  }
   const int H = a.hidden, nb = a.nb_h;
   int P2 = 1;
   while (P2 < nb) P2 <<= 1;
@@ -112,21 +132,6 @@ __global__ __launch_bounds__(128 * Q) void k_route(DecodeArgs a) {
     double lg[1];
     router_wave<1>(a.w_router, xt, 1, H, a.bias, e, 0, lane, lg);
     if (lane == 0) a.logits[(size_t)t * a.E + e] = lg[0];
-  }
-  // this workgroup's share of the int8 token quantization: two blocks per wave
-  // pass, one per half-wave
-  const int nblk = a.q * nb;
-  const int b_end = min((int)(blockIdx.x + 1) * a.quant_per_wg, nblk);
-  for (int b0 = blockIdx.x * a.quant_per_wg + 2 * w; b0 < b_end; b0 += 4 * Q) {
-    const int b = b0 + (lane >> 5), j = lane & 31;
-    const bool ok = b < b_end;
-    const float v = ok ? a.x[(size_t)b * 32 + j] : 0.0f;
-    float d;
-    const uint32_t qw = quant_block32_lanes(v, a.rot_gateup, &d);
-    if (ok) {
-      if ((j & 3) == 0) reinterpret_cast<uint32_t*>(a.xq + (size_t)b * 32)[j >> 2] = qw;
-      if (j == 0) a.dx[b] = d;
-    }
   }
 }
 
@@ -798,7 +803,9 @@ __global__ __launch_bounds__(256) void k_down1(DecodeArgs a) {
 template <int FG, int FD, int Q>
 int launch_decode_t(const DecodeArgs& a, int U_max, hipStream_t s) {
   {
-    launch_kernel("route", k_route<Q>, dim3(a.E), dim3(128 * Q), s, a);
+    // E logit workgroups, then the token-quantization workgroups
+    const int nq = (a.q * a.nb_h + a.quant_per_wg - 1) / a.quant_per_wg;
+    launch_kernel("route", k_route<Q>, dim3(a.E + nq), dim3(128 * Q), s, a);
   }
   int st = launch_check("route");
   if (st) return st;
@@ -889,7 +896,7 @@ extern "C" int qmoe_decode_layer(const qmoe_layer* L, const float* x, int32_t q,
   a.dn_row_bytes = (size_t)a.nb_i * fd.block_bytes;
   a.dn_stride = a.dn_row_bytes * L->hidden;
   a.dn_lpr_log2 = ilog2(lanes_per_row(a.nb_i, L->fmt_down == QMOE_FP4 ? 1 : 2));
-  a.quant_per_wg = (q * a.nb_h + L->n_experts - 1) / L->n_experts;
+  a.quant_per_wg = 4 * q;   // blocks per token-quantization workgroup: one pass of its half-waves
   const int U_max = std::min(q * L->topk, L->n_experts);
   hipStream_t s = as_stream(stream);
   switch (q) {
