@@ -288,6 +288,10 @@ __device__ __forceinline__ void gateup_epilogue(const DecodeArgs& a, uint32_t ma
                                                 const float (&ag)[RPW][Q], const float (&au)[RPW][Q],
                                                 float (&s_a)[4][32]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // every lane ends with every row sum; lane k then forms the SwiGLU of value
+  // k = r * Q + t, so the RPW * Q exp / divide sequences take one pass of the
+  // wave instead of one pass each (the same fp32 operations per value)
+  float gk = 0.0f, uk = 0.0f;
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
@@ -295,8 +299,15 @@ __device__ __forceinline__ void gateup_epilogue(const DecodeArgs& a, uint32_t ma
       if (mask >> t & 1) {
         const float gv = group_sum(ag[r][t], 64);
         const float uv = group_sum(au[r][t], 64);
-        if (lane == 0) s_a[t][wave * RPW + r] = gv / (1.0f + expf(-gv)) * uv;
+        if (lane == r * Q + t) {
+          gk = gv;
+          uk = uv;
+        }
       }
+  if (lane < RPW * Q) {
+    const int r = lane / Q, t = lane % Q;
+    if (mask >> t & 1) s_a[t][wave * RPW + r] = gk / (1.0f + expf(-gk)) * uk;
+  }
   __syncthreads();
   // requantize the 32-row block: half-wave h of wave w takes column 2w + h
   if (wave < (Q + 1) / 2) {
