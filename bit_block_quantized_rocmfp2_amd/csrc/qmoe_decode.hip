@@ -276,6 +276,64 @@ __device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, in
   }
 }
 
+// ------------------------------------------------------------ wave sums of many values
+// Value of lane l ^ M (all 64 lanes active): DPP quad permutes for M = 1, 2, a
+// row rotation by 8 (lane ^ 8 inside a 16-lane row) for M = 8, ds_swizzle for
+// M = 4 and 16, a permute across the halves for M = 32.
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (M == 1 || M == 2) return xchg32<M>(v);
+  else if constexpr (M == 8) return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+  else if constexpr (M == 4 || M == 16) return xchg32<M>(v);
+  else return __shfl_xor(v, 32);
+}
+
+// One transposing step at stride M: lane l holds values a (lower) and b (upper)
+// and returns a(l) + a(l ^ M) if lane & M is clear, b(l) + b(l ^ M) if it is set.
+// For M = 32 and 16 this is one v_permlane32_swap / v_permlane16_swap, which
+// exchanges the upper lanes (odd 16-lane rows) of its first operand with the
+// lower lanes (even rows) of its second, so each lane then holds its own and
+// its partner's copy of the half it keeps.
+template <int M>
+__device__ __forceinline__ float tstep(float a, float b, bool hi) {
+  if constexpr (M == 32 || M == 16) {
+    const auto r = (M == 32) ? __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false)
+                             : __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    const float keep = hi ? b : a, send = hi ? a : b;
+    return keep + lane_xor<M>(send);
+  }
+}
+
+// Sums N values per lane (N a power of two) over the wave by a transposing
+// butterfly: at stride M = 32, 16, ... while a lane holds more than one value,
+// it keeps half of them (the upper half when lane & M is set) and adds the
+// partner's copy of that half; once one value remains, plain butterflies finish.
+// Every value is summed in pairs at strides 32, 16, 8, 4, 2, 1 (the same tree
+// for any N, and IEEE addition is commutative, so the order of the two
+// operands does not matter). On return v[0] is the sum of value k, with k built
+// from the lane bits of the transposing strides (the same k for equal N).
+template <int N, int M>
+__device__ __forceinline__ void wave_tsum(float* v, int lane, int& k) {
+  if constexpr (M >= 1) {
+    if constexpr (N > 1) {
+      constexpr int H = N / 2;
+      const bool hi = (lane & M) != 0;
+#pragma unroll
+      for (int i = 0; i < H; ++i) v[i] = tstep<M>(v[i], v[i + H], hi);
+      if (hi) k += H;
+      wave_tsum<H, M / 2>(v, lane, k);
+    } else {
+      v[0] = v[0] + lane_xor<M>(v[0]);
+      wave_tsum<1, M / 2>(v, lane, k);
+    }
+  }
+}
+
+constexpr int pow2_at_least(int n) { return n <= 1 ? 1 : 2 * pow2_at_least((n + 1) / 2); }
+constexpr int log2_exact(int n) { return n <= 1 ? 0 : 1 + log2_exact(n / 2); }
+
 // ------------------------------------------------------------ k_gateup
 // 8 waves; wave w owns rows 4w..4w+3 of both gate and up of the workgroup's 32
 // rows. Lanes cover NBL consecutive blocks each.
@@ -288,25 +346,24 @@ __device__ __forceinline__ void gateup_epilogue(const DecodeArgs& a, uint32_t ma
                                                 const float (&ag)[RPW][Q], const float (&au)[RPW][Q],
                                                 float (&s_a)[4][32]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // every lane ends with every row sum; lane k then forms the SwiGLU of value
-  // k = r * Q + t, so the RPW * Q exp / divide sequences take one pass of the
-  // wave instead of one pass each (the same fp32 operations per value)
-  float gk = 0.0f, uk = 0.0f;
+  // the RPW * Q gate and up row sums over the wave, by transposing butterflies
+  // with one lane mapping: lane l ends with the gate and up sums of value
+  // k = r * Q + t, and the first lane of each group forms its SwiGLU (all values
+  // in one pass of the wave)
+  constexpr int NV = RPW * Q, NP = pow2_at_least(NV);
+  float g[NP], uu[NP];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r)
-#pragma unroll
-    for (int t = 0; t < Q; ++t)
-      if (mask >> t & 1) {
-        const float gv = group_sum(ag[r][t], 64);
-        const float uv = group_sum(au[r][t], 64);
-        if (lane == r * Q + t) {
-          gk = gv;
-          uk = uv;
-        }
-      }
-  if (lane < RPW * Q) {
-    const int r = lane / Q, t = lane % Q;
-    if (mask >> t & 1) s_a[t][wave * RPW + r] = gk / (1.0f + expf(-gk)) * uk;
+  for (int i = 0; i < NP; ++i) {
+    g[i] = (i < NV) ? ag[i / Q][i % Q] : 0.0f;
+    uu[i] = (i < NV) ? au[i / Q][i % Q] : 0.0f;
+  }
+  int kg = 0, ku = 0;
+  wave_tsum<NP, 32>(g, lane, kg);
+  wave_tsum<NP, 32>(uu, lane, ku);
+  constexpr int GROUP = 64 >> log2_exact(NP);   // lanes holding the same value
+  if ((lane & (GROUP - 1)) == 0 && kg < NV) {
+    const int r = kg / Q, t = kg % Q;
+    if (mask >> t & 1) s_a[t][wave * RPW + r] = g[0] / (1.0f + expf(-g[0])) * uu[0];
   }
   __syncthreads();
   // requantize the 32-row block: half-wave h of wave w takes column 2w + h
