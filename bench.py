@@ -334,6 +334,29 @@ def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
                              "frac_hbm_peak": round(gbs4 / HBM_PEAK_GBS, 4)}
     log(f"decode q=1 top-4: {ms4 * 1e3:.2f} us/call, {gbs4:.1f} GB/s")
 
+    # format variant: the same layer with FP2 down projections (2.5 bits per weight
+    # everywhere), q = 1; gate/up and the router are shared with the FP3-down layer
+    spec2 = gen.LayerSpec.full(fmt_down=2)
+    down2, cb_down2 = qm.device.pack_experts(spec2, "down", 0, dev)
+    desc2 = qm.make_layer(spec2.hidden, spec2.inter, spec2.n_experts, spec2.topk, spec2.fmt_gate, spec2.fmt_up,
+                          spec2.fmt_down, spec2.rot_gateup, spec2.rot_down, dl.w_router, None, dl.gate, dl.up, down2,
+                          dl.cb_gate, dl.cb_up, cb_down2)
+    qm.qmoe_layer_check(desc2)
+    per_expert2 = (qm.qmoe_packed_bytes(2, spec2.inter, spec2.hidden) * 2
+                   + qm.qmoe_packed_bytes(2, spec2.hidden, spec2.inter))
+    for i in range(10):
+        qm.qmoe_decode_layer(desc2, toks[i % 64: i % 64 + 1], out[:1], ws)
+    with Timer(torch) as t2:
+        for i in range(K):
+            qm.qmoe_decode_layer(desc2, toks[i % 64: i % 64 + 1], out[:1], ws)
+    ms2 = t2.ms / K
+    gbs2 = spec2.topk * per_expert2 / (ms2 * 1e-3) / 1e9
+    res["decode_q1_fp2_down"] = {"us_per_call": round(ms2 * 1e3, 2), "effective_GBps": round(gbs2, 1),
+                                 "frac_hbm_peak": round(gbs2 / HBM_PEAK_GBS, 4),
+                                 "packed_bytes_per_call": spec2.topk * per_expert2}
+    log(f"decode q=1 FP2 down: {ms2 * 1e3:.2f} us/call, {gbs2:.1f} GB/s")
+    del down2, cb_down2
+
     # ---------------------------------------------------------------- prefill 8K (Zipf)
     try:
         res["prefill_8k"] = bench_prefill(torch, qm, gen, spec, dl, dev)

@@ -27,6 +27,30 @@ def to_device(a: np.ndarray, device="cuda"):
     return torch.from_numpy(a).to(device)
 
 
+def pack_experts(spec, name: str, seed: int = 0, device="cuda", workers: int = 0):
+    """One projection ("gate", "up" or "down") of every expert of a layer, packed
+    in the spec's format and copied to the GPU: (packed bytes, codebooks)."""
+    from synth import gen
+    torch = _torch()
+    E = spec.n_experts
+    rows, k, fmt = spec.shape(name)
+    row_bytes = B.qmoe_packed_bytes(fmt, 1, k)
+    host = np.empty((E, rows * row_bytes), dtype=np.uint8)
+    cb = np.empty((E, 1 << fmt), dtype=np.int8)
+
+    def work(e):
+        t = gen.expert_tensor(spec, name, e, seed)
+        host[e] = B.qmoe_pack(fmt, t.codes, t.scales).reshape(-1)
+        cb[e] = t.cb
+
+    nw = workers or min(16, os.cpu_count() or 4)
+    with cf.ThreadPoolExecutor(nw) as ex:
+        list(ex.map(work, range(E)))
+    packed = torch.from_numpy(host.reshape(-1)).to(device)
+    del host
+    return packed, torch.from_numpy(cb.reshape(-1)).to(device)
+
+
 class DeviceLayer:
     """All experts of one MoE layer packed and copied to the GPU."""
 
@@ -35,26 +59,10 @@ class DeviceLayer:
         torch = _torch()
         self.spec = spec
         self.seed = seed
-        E = spec.n_experts
         tensors = {}
         cbs = {}
         for name in ("gate", "up", "down"):
-            rows, k, fmt = spec.shape(name)
-            row_bytes = B.qmoe_packed_bytes(fmt, 1, k)
-            host = np.empty((E, rows * row_bytes), dtype=np.uint8)
-            cb = np.empty((E, 1 << fmt), dtype=np.int8)
-
-            def work(e, name=name, fmt=fmt, host=host, cb=cb):
-                t = gen.expert_tensor(spec, name, e, seed)
-                host[e] = B.qmoe_pack(fmt, t.codes, t.scales).reshape(-1)
-                cb[e] = t.cb
-
-            nw = workers or min(16, os.cpu_count() or 4)
-            with cf.ThreadPoolExecutor(nw) as ex:
-                list(ex.map(work, range(E)))
-            tensors[name] = torch.from_numpy(host.reshape(-1)).to(device)
-            del host
-            cbs[name] = torch.from_numpy(cb.reshape(-1)).to(device)
+            tensors[name], cbs[name] = pack_experts(spec, name, seed, device, workers)
         self.gate, self.up, self.down = tensors["gate"], tensors["up"], tensors["down"]
         self.cb_gate, self.cb_up, self.cb_down = cbs["gate"], cbs["up"], cbs["down"]
         self.w_router_host = gen.router_weights(spec, seed)

@@ -322,6 +322,24 @@ def test_decode_tiny(q, rots):
     assert np.array_equal(gidx, idx)
 
 
+@pytest.mark.parametrize("q", [1, 4])
+@pytest.mark.parametrize("fg,fd", [(2, 2), (2, 4), (3, 3), (3, 2), (4, 2), (4, 4)])
+def test_decode_formats(fg, fd, q):
+    """Other format pairings of the same layer: gate/up in ROCmFP2/3/4 with the
+    down projection in FP2 (the 2-bit down of the selected layers), FP3 or FP4.
+    Routing ids bit-exact, output within the layer tolerance."""
+    spec = gen.LayerSpec(hidden=512, inter=512, n_experts=16, topk=4, fmt_gate=fg, fmt_up=fg, fmt_down=fd,
+                         rot_down=1 if fd == 2 else 0)
+    dl = qm.device.DeviceLayer(spec, seed=18)
+    x = gen.tokens(q, spec.hidden, seed=180 + q)
+    out, ws = run_decode(dl, x)
+    ref, idx_ref, _ = moe.moe_tokens(oracle_layer(spec, 18, dl.w_router_host), x)
+    lay = qm.qmoe_workspace_layout(dl.desc, q)
+    idx = ws[lay["idx"]: lay["idx"] + 4 * q * spec.topk].cpu().numpy().view(np.int32).reshape(q, spec.topk)
+    assert np.array_equal(idx, idx_ref)
+    assert moe.rel_l2(out, ref) < TOL
+
+
 def test_decode_ragged_shapes():
     """hidden 768 (a partial 128-block chunk), 12 experts, top-3, biased router."""
     spec = gen.LayerSpec(hidden=768, inter=512, n_experts=12, topk=3, rot_down=1)

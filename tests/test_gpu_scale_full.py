@@ -88,6 +88,46 @@ def test_full_decode_q1_top4(full):
         assert moe.rel_l2(out.cpu().numpy(), ref) < TOL
 
 
+def test_full_decode_fp2_down(full):
+    """The full layer with its down projections in ROCmFP2 (gate/up and router
+    shared), in the launch configuration the benchmark times: q = 1 (one
+    pass of the lanes over the FP2 rows) and q = 4. Ids bit-exact, output
+    within the tolerance."""
+    spec, dl, L3 = full
+    spec2 = gen.LayerSpec.full(fmt_down=2)
+    down2, cb_down2 = qm.device.pack_experts(spec2, "down", SEED)
+    desc2 = qm.make_layer(spec2.hidden, spec2.inter, spec2.n_experts, spec2.topk, spec2.fmt_gate, spec2.fmt_up,
+                          spec2.fmt_down, spec2.rot_gateup, spec2.rot_down, dl.w_router, None, dl.gate, dl.up, down2,
+                          dl.cb_gate, dl.cb_up, cb_down2)
+    qm.qmoe_layer_check(desc2)
+    cache = {}
+
+    def get(name, e):
+        if name != "down":
+            return L3.get(name, e)
+        if e not in cache:
+            t = gen.expert_tensor(spec2, "down", e, SEED)
+            cache[e] = (t.fmt, t.codes, t.scales, t.cb)
+        return cache[e]
+
+    L2 = moe.Layer(spec2.hidden, spec2.inter, spec2.n_experts, spec2.topk, dl.w_router_host, get)
+    for q in (1, 4):
+        x = gen.tokens(q, spec2.hidden, seed=SEED + 5, stream=3)
+        xd = qm.device.to_device(x)
+        out = torch.empty_like(xd)
+        ws = torch.zeros(qm.qmoe_workspace_bytes(desc2, q), dtype=torch.uint8, device="cuda")
+        qm.qmoe_decode_layer(desc2, xd, out, ws)
+        torch.cuda.synchronize()
+        lay = qm.qmoe_workspace_layout(desc2, q)
+        k = spec2.topk
+        idx = ws[lay["idx"]: lay["idx"] + q * k * 4].cpu().numpy().view(np.int32).reshape(q, k)
+        ref, idx_ref, _ = moe.moe_tokens(L2, x)
+        assert np.array_equal(idx, idx_ref)
+        err = moe.rel_l2(out.cpu().numpy(), ref)
+        print(f"FP2 down q={q}: rel_l2 {err:.2e}")
+        assert err < TOL
+
+
 def test_full_decode_q4_forced_overlap(full):
     spec, dl, L = full
     for variant in range(64):
