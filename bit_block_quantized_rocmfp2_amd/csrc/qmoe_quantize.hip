@@ -20,8 +20,10 @@
 //                starting centroids.
 //   k_qz_assign  one Lloyd assignment pass: G workgroups per matrix stream its
 //                v, each lane keeps per-entry sums and counts in LDS slots of
-//                its own (no contention), and each workgroup writes its integer
-//                partial sums; no atomics.
+//                its own (no contention; with 4 sorted entries, in registers
+//                as sums above each threshold, from packed int16 arithmetic),
+//                and each workgroup writes its integer partial sums; no
+//                global atomics.
 //   k_qz_update  one workgroup per matrix: adds the G partials of each entry
 //                (exact integers) and moves the centroid to the mean rounded
 //                half up (floor division); an entry with no members keeps its
@@ -189,6 +191,61 @@ __device__ __forceinline__ void qz_assign_loop(const u32x4* __restrict__ src, si
   }
 }
 
+typedef short qz_i16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short qz_u16x2 __attribute__((ext_vector_type(2)));
+
+// The sorted rule without per-value slots: a value x goes above threshold i
+// (entry index > i) exactly when 2x > mid[i], i.e. x > h[i] = floor(mid[i] / 2)
+// for integer x. Per pair of int16 values (one dword) and threshold: the
+// saturating packed difference h - x is negative exactly when x > h, so its
+// sign bit is the 0/1 indicator of each half; two integer dot products add the
+// indicated values and the indicators. The thread ends with, per threshold,
+// the sum and count of its values above it, plus the sum of all its values;
+// the per-entry sums and counts are the differences of consecutive ones (exact
+// integer arithmetic, the same totals as one slot per entry).
+template <int NC>
+__device__ __forceinline__ void qz_assign_sorted_pairs(const u32x4* __restrict__ src, size_t npieces, size_t first,
+                                                       size_t stride, const int (&mid)[NC - 1],
+                                                       int (&s_sum)[NC][256], int (&s_cnt)[NC][256]) {
+  const int tid = threadIdx.x;
+  qz_i16x2 h[NC - 1];
+#pragma unroll
+  for (int i = 0; i < NC - 1; ++i) {
+    const short hi = (short)(mid[i] >> 1);   // floor division by 2; |mid| <= 65534
+    h[i] = qz_i16x2{hi, hi};
+  }
+  const qz_i16x2 one = {1, 1};
+  int above_sum[NC - 1], above_cnt[NC - 1], total = 0, n = 0;
+#pragma unroll
+  for (int i = 0; i < NC - 1; ++i) above_sum[i] = above_cnt[i] = 0;
+  for (size_t p = first; p < npieces; p += stride) {
+    const u32x4 r = src[p];
+    const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const qz_i16x2 x = __builtin_bit_cast(qz_i16x2, wd[d]);
+      total = __builtin_amdgcn_sdot2(x, one, total, false);
+#pragma unroll
+      for (int i = 0; i < NC - 1; ++i) {
+        const qz_i16x2 nd = __builtin_elementwise_sub_sat(h[i], x);
+        const qz_u16x2 ind = __builtin_bit_cast(qz_u16x2, nd) >> (qz_u16x2){15, 15};
+        above_sum[i] = __builtin_amdgcn_sdot2(x, __builtin_bit_cast(qz_i16x2, ind), above_sum[i], false);
+        above_cnt[i] = __builtin_amdgcn_sdot2(__builtin_bit_cast(qz_i16x2, ind), one, above_cnt[i], false);
+      }
+    }
+    n += 8;
+  }
+  s_sum[0][tid] = total - above_sum[0];
+  s_cnt[0][tid] = n - above_cnt[0];
+#pragma unroll
+  for (int i = 1; i < NC - 1; ++i) {
+    s_sum[i][tid] = above_sum[i - 1] - above_sum[i];
+    s_cnt[i][tid] = above_cnt[i - 1] - above_cnt[i];
+  }
+  s_sum[NC - 1][tid] = above_sum[NC - 2];
+  s_cnt[NC - 1][tid] = above_cnt[NC - 2];
+}
+
 // Q3, assignment: grid (G, n). Lane slots s_sum/s_cnt[entry][thread] hold this
 // thread's sums (at most 8 * 32767 per piece, so int32 is exact per slot up to
 // 2^31 / 32767 = 65538 values per thread) and counts. Lloyd's iterations keep
@@ -216,7 +273,9 @@ __global__ __launch_bounds__(256) void k_qz_assign(const int16_t* __restrict__ v
   const u32x4* src = reinterpret_cast<const u32x4*>(v + (size_t)m * per_mat);
   const size_t npieces = per_mat / 8;   // 8 values per 16-byte piece
   const size_t first = (size_t)blockIdx.x * 256 + tid, stride = (size_t)G * 256;
-  if (inc)
+  if (inc && NC == 4)
+    qz_assign_sorted_pairs<NC>(src, npieces, first, stride, mid, s_sum, s_cnt);
+  else if (inc)
     qz_assign_loop<NC, true>(src, npieces, first, stride, cc, mid, s_sum, s_cnt);
   else
     qz_assign_loop<NC, false>(src, npieces, first, stride, cc, mid, s_sum, s_cnt);
