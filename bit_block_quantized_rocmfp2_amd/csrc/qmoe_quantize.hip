@@ -218,22 +218,35 @@ __device__ __forceinline__ void qz_assign_sorted_pairs(const u32x4* __restrict__
   int above_sum[NC - 1], above_cnt[NC - 1], total = 0, n = 0;
 #pragma unroll
   for (int i = 0; i < NC - 1; ++i) above_sum[i] = above_cnt[i] = 0;
-  for (size_t p = first; p < npieces; p += stride) {
-    const u32x4 r = src[p];
-    const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+  // four pieces in flight per lane: every load is issued (index clamped into
+  // range) before any is used; pieces past the end are loaded but not counted
+  constexpr int PF = 4;
+  for (size_t p0 = first; p0 < npieces; p0 += PF * stride) {
+    u32x4 r[PF];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const qz_i16x2 x = __builtin_bit_cast(qz_i16x2, wd[d]);
-      total = __builtin_amdgcn_sdot2(x, one, total, false);
+    for (int k = 0; k < PF; ++k) r[k] = src[min(p0 + k * stride, npieces - 1)];
+    // an empty asm that takes every loaded piece keeps the compiler from sinking
+    // the later loads into the branches that use them (one round trip each)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::"v"(r[0]), "v"(r[1]), "v"(r[2]), "v"(r[3]));
 #pragma unroll
-      for (int i = 0; i < NC - 1; ++i) {
-        const qz_i16x2 nd = __builtin_elementwise_sub_sat(h[i], x);
-        const qz_u16x2 ind = __builtin_bit_cast(qz_u16x2, nd) >> (qz_u16x2){15, 15};
-        above_sum[i] = __builtin_amdgcn_sdot2(x, __builtin_bit_cast(qz_i16x2, ind), above_sum[i], false);
-        above_cnt[i] = __builtin_amdgcn_sdot2(__builtin_bit_cast(qz_i16x2, ind), one, above_cnt[i], false);
+    for (int k = 0; k < PF; ++k) {
+      if (p0 + k * stride >= npieces) break;
+      const uint32_t wd[4] = {r[k].x, r[k].y, r[k].z, r[k].w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const qz_i16x2 x = __builtin_bit_cast(qz_i16x2, wd[d]);
+        total = __builtin_amdgcn_sdot2(x, one, total, false);
+#pragma unroll
+        for (int i = 0; i < NC - 1; ++i) {
+          const qz_i16x2 nd = __builtin_elementwise_sub_sat(h[i], x);
+          const qz_u16x2 ind = __builtin_bit_cast(qz_u16x2, nd) >> (qz_u16x2){15, 15};
+          above_sum[i] = __builtin_amdgcn_sdot2(x, __builtin_bit_cast(qz_i16x2, ind), above_sum[i], false);
+          above_cnt[i] = __builtin_amdgcn_sdot2(__builtin_bit_cast(qz_i16x2, ind), one, above_cnt[i], false);
+        }
       }
+      n += 8;
     }
-    n += 8;
   }
   s_sum[0][tid] = total - above_sum[0];
   s_cnt[0][tid] = n - above_cnt[0];
