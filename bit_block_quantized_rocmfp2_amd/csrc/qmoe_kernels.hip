@@ -208,10 +208,10 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits,
 // ------------------------------------------------------------ dense matvec (1..4 columns)
 // Each wave handles 64/LPR rows at once (LPR lanes per row, NBL blocks per lane).
 template <int FMT, int Q, int UF>
-__global__ __launch_bounds__(256) void k_matvec(const uint8_t* __restrict__ W, int64_t rows, size_t row_bytes, int nb,
-                                                int lpr_log2, const int8_t* __restrict__ cbp,
-                                                const int8_t* __restrict__ xq, const float* __restrict__ dx,
-                                                float* __restrict__ y) {
+__device__ __forceinline__ void matvec_body(const uint8_t* __restrict__ W, int64_t rows, size_t row_bytes, int nb,
+                                            int lpr_log2, const int8_t* __restrict__ cbp,
+                                            const int8_t* __restrict__ xq, const float* __restrict__ dx,
+                                            float* __restrict__ y) {
   constexpr int NBL = (FMT == 4) ? 1 : 2;
   const int lpr = 1 << lpr_log2;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -263,6 +263,67 @@ __global__ __launch_bounds__(256) void k_matvec(const uint8_t* __restrict__ W, i
     const float v = group_sum(acc[t], lpr);
     if (sl == 0 && row_ok) y[(size_t)t * rows + row] = v;
   }
+}
+
+template <int FMT, int Q, int UF>
+__global__ __launch_bounds__(256) void k_matvec(const uint8_t* __restrict__ W, int64_t rows, size_t row_bytes, int nb,
+                                                int lpr_log2, const int8_t* __restrict__ cbp,
+                                                const int8_t* __restrict__ xq, const float* __restrict__ dx,
+                                                float* __restrict__ y) {
+  matvec_body<FMT, Q, UF>(W, rows, row_bytes, nb, lpr_log2, cbp, xq, dx, y);
+}
+
+// The same matvec with the activation quantization in the launch, when the
+// columns hold at most kFqMaxBlocks blocks in all: every workgroup quantizes
+// them itself (32 lanes per block, two blocks per wave pass, the same IEEE
+// operations as k_quant_act) into LDS, with all of a wave's loads in flight at
+// once, which costs less than the separate launch it replaces; workgroup 0 also
+// writes the int8 values and scales to xq_out / dx_out, as the two-launch form
+// leaves them. With more blocks (four columns of 2048 values: 256) the
+// redundant quantization costs more than the launch.
+constexpr int kFqMaxBlocks = 64;
+constexpr int kFqBatch = kFqMaxBlocks / 8;   // passes of the workgroup
+
+template <int FMT, int Q, int UF>
+__global__ __launch_bounds__(256) void k_matvec_fq(const uint8_t* __restrict__ W, int64_t rows, size_t row_bytes,
+                                                   int nb, int lpr_log2, const int8_t* __restrict__ cbp,
+                                                   const float* __restrict__ x, int rot, int8_t* __restrict__ xq_out,
+                                                   float* __restrict__ dx_out, float* __restrict__ y) {
+  __shared__ __align__(16) int8_t s_xq[kFqMaxBlocks * 32];
+  __shared__ float s_dx[kFqMaxBlocks];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane & 31;
+  const int nblk = Q * nb;             // <= kFqMaxBlocks
+  const int npass = (nblk + 7) / 8;   // 8 blocks per pass of the workgroup, <= kFqBatch
+  const bool writer = blockIdx.x == 0;
+  for (int p0 = 0; p0 < npass; p0 += kFqBatch) {
+    float v[kFqBatch];
+#pragma unroll
+    for (int k = 0; k < kFqBatch; ++k) {
+      const int i = min(((p0 + k) * 4 + wave) * 2 + (lane >> 5), nblk - 1);
+      v[k] = x[(size_t)i * 32 + j];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < kFqBatch; ++k) {
+      if (p0 + k >= npass) break;   // wave-uniform
+      const int i = ((p0 + k) * 4 + wave) * 2 + (lane >> 5);
+      float d;
+      const uint32_t packed = quant_block32_lanes(v[k], rot, &d);
+      if (i < nblk) {
+        if ((j & 3) == 0) {
+          *reinterpret_cast<uint32_t*>(&s_xq[i * 32 + j]) = packed;
+          if (writer) *reinterpret_cast<uint32_t*>(xq_out + (size_t)i * 32 + j) = packed;
+        }
+        if (j == 0) {
+          s_dx[i] = d;
+          if (writer) dx_out[i] = d;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  matvec_body<FMT, Q, UF>(W, rows, row_bytes, nb, lpr_log2, cbp, s_xq, s_dx, y);
 }
 
 // ------------------------------------------------------------ expand-then-multiply (comparison path)
@@ -485,6 +546,32 @@ void launch_matvec_t(const uint8_t* W, int64_t rows, size_t row_bytes, int nb, i
                   lpr_log2, cb, xq, dx, y);
 }
 
+template <int FMT, int Q>
+void launch_matvec_fq_t(const uint8_t* W, int64_t rows, size_t row_bytes, int nb, int lpr_log2, const int8_t* cb,
+                        const float* x, int rot, int8_t* xq, float* dx, float* y, hipStream_t s) {
+  const int rows_per_wg = 4 * (64 >> lpr_log2);
+  const unsigned grid = (unsigned)((rows + rows_per_wg - 1) / rows_per_wg);
+  constexpr int NBL = (FMT == 4) ? 1 : 2;
+  const int chunks = (nb + (NBL << lpr_log2) - 1) / (NBL << lpr_log2);
+  if (chunks == 1)
+    launch_kernel("matvec_fq", k_matvec_fq<FMT, Q, 1>, dim3(grid), dim3(256), s, W, rows, row_bytes, nb, lpr_log2,
+                  cb, x, rot, xq, dx, y);
+  else
+    launch_kernel("matvec_fq", k_matvec_fq<FMT, Q, (Q <= 2) ? 4 : 2>, dim3(grid), dim3(256), s, W, rows, row_bytes,
+                  nb, lpr_log2, cb, x, rot, xq, dx, y);
+}
+
+template <int FMT>
+void launch_matvec_fq_f(int q, const uint8_t* W, int64_t rows, size_t row_bytes, int nb, int lpr_log2,
+                        const int8_t* cb, const float* x, int rot, int8_t* xq, float* dx, float* y, hipStream_t s) {
+  switch (q) {
+    case 1: launch_matvec_fq_t<FMT, 1>(W, rows, row_bytes, nb, lpr_log2, cb, x, rot, xq, dx, y, s); break;
+    case 2: launch_matvec_fq_t<FMT, 2>(W, rows, row_bytes, nb, lpr_log2, cb, x, rot, xq, dx, y, s); break;
+    case 3: launch_matvec_fq_t<FMT, 3>(W, rows, row_bytes, nb, lpr_log2, cb, x, rot, xq, dx, y, s); break;
+    default: launch_matvec_fq_t<FMT, 4>(W, rows, row_bytes, nb, lpr_log2, cb, x, rot, xq, dx, y, s); break;
+  }
+}
+
 template <int FMT>
 void launch_matvec_f(int q, const uint8_t* W, int64_t rows, size_t row_bytes, int nb, int lpr_log2,
                      const int8_t* cb, const int8_t* xq, const float* dx, float* y, hipStream_t s) {
@@ -571,11 +658,19 @@ extern "C" int qmoe_matvec(int fmt, int64_t rows, int64_t k, const void* w, size
   float* dx = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + round_up((size_t)ncols * k, 256));
   hipStream_t s = as_stream(stream);
   const int nb = (int)(k / 32);
-  if ((st = launch_quant(x, (int64_t)ncols * nb, rot, xq, dx, s))) return st;
   const int nbl = fmt == 4 ? 1 : 2;
   const int lg = ilog2(lanes_per_row(nb, nbl));
   const size_t row_bytes = (size_t)nb * fi.block_bytes;
   const uint8_t* W = static_cast<const uint8_t*>(w);
+  if ((int64_t)ncols * nb <= kFqMaxBlocks) {   // one launch: quantization inside the matvec
+    switch (fmt) {
+      case 2: launch_matvec_fq_f<2>(ncols, W, rows, row_bytes, nb, lg, cb, x, rot, xq, dx, y, s); break;
+      case 3: launch_matvec_fq_f<3>(ncols, W, rows, row_bytes, nb, lg, cb, x, rot, xq, dx, y, s); break;
+      default: launch_matvec_fq_f<4>(ncols, W, rows, row_bytes, nb, lg, cb, x, rot, xq, dx, y, s); break;
+    }
+    return launch_check("matvec_fq");
+  }
+  if ((st = launch_quant(x, (int64_t)ncols * nb, rot, xq, dx, s))) return st;
   switch (fmt) {
     case 2: launch_matvec_f<2>(ncols, W, rows, row_bytes, nb, lg, cb, xq, dx, y, s); break;
     case 3: launch_matvec_f<3>(ncols, W, rows, row_bytes, nb, lg, cb, xq, dx, y, s); break;
