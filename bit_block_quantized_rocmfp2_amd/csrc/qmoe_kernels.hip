@@ -206,8 +206,13 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits,
 }
 
 // ------------------------------------------------------------ dense matvec (1..4 columns)
-// Each wave handles 64/LPR rows at once (LPR lanes per row, NBL blocks per lane).
-template <int FMT, int Q, int UF>
+// Each wave handles 64/LPR rows at once (LPR lanes per row, NBL blocks per lane),
+// R times: the R row groups of a wave use the same lanes for the same blocks,
+// so each activation load serves R rows (with one row per wave and long rows,
+// the activations read from L2 otherwise outweigh the weights several times
+// at four columns). Each row's lane mapping and accumulation order do not
+// depend on R.
+template <int FMT, int Q, int UF, int R = 1>
 __device__ __forceinline__ void matvec_body(const uint8_t* __restrict__ W, int64_t rows, size_t row_bytes, int nb,
                                             int lpr_log2, const int8_t* __restrict__ cbp,
                                             const int8_t* __restrict__ xq, const float* __restrict__ dx,
@@ -217,25 +222,34 @@ __device__ __forceinline__ void matvec_body(const uint8_t* __restrict__ W, int64
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int sub = lane >> lpr_log2, sl = lane & (lpr - 1);
   const int rows_per_wave = 64 >> lpr_log2;
-  const int64_t row = ((int64_t)blockIdx.x * 4 + wave) * rows_per_wave + sub;
-  const bool row_ok = row < rows;
+  int64_t row[R];
+  bool row_ok[R];
+  const uint8_t* rowp[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    row[r] = (((int64_t)blockIdx.x * 4 + wave) * R + r) * rows_per_wave + sub;
+    row_ok[r] = row[r] < rows;
+    rowp[r] = W + (size_t)(row_ok[r] ? row[r] : rows - 1) * row_bytes;
+  }
   uint32_t cb[4];
   load_codebook<FMT>(cbp, cb);
-  float acc[Q];
+  float acc[R][Q];
 #pragma unroll
-  for (int t = 0; t < Q; ++t) acc[t] = 0.0f;
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < Q; ++t) acc[r][t] = 0.0f;
   // UF chunks of the row (lpr * NBL blocks each) per step: the loads of all UF
   // chunks are issued (clamped into range) before any is used, so a wave makes
   // one memory round trip per UF chunks; the products are taken chunk by chunk
   // in ascending order, as a one-chunk loop would (UF = 1 when a row is one chunk)
-  const uint8_t* rowp = W + (size_t)(row_ok ? row : rows - 1) * row_bytes;
   for (int c0 = 0; c0 < nb; c0 += UF * lpr * NBL) {
-    Blocks<FMT, NBL> bl[UF];
+    Blocks<FMT, NBL> bl[UF][R];
     Acts<NBL> act[UF][Q];
 #pragma unroll
     for (int u = 0; u < UF; ++u) {
       const int bc = min(c0 + u * lpr * NBL + sl * NBL, nb - NBL);
-      bl[u].load(rowp, nb, bc);
+#pragma unroll
+      for (int r = 0; r < R; ++r) bl[u][r].load(rowp[r], nb, bc);
 #pragma unroll
       for (int t = 0; t < Q; ++t) act[u][t].load(xq + (size_t)t * nb * 32, dx + (size_t)t * nb, bc);
     }
@@ -243,34 +257,40 @@ __device__ __forceinline__ void matvec_body(const uint8_t* __restrict__ W, int64
 #pragma unroll
     for (int u = 0; u < UF; ++u) {
       const int b = c0 + u * lpr * NBL + sl * NBL;
-      if (row_ok && b < nb) {
+      if (b < nb) {
 #pragma unroll
-        for (int i = 0; i < NBL; ++i) {
-          uint32_t w[8];
-          bl[u].expand(i, cb, w);
-          const float s = bl[u].scale(i);
+        for (int r = 0; r < R; ++r)
+          if (row_ok[r]) {
 #pragma unroll
-          for (int t = 0; t < Q; ++t) {
-            const int p = block_dot(w, act[u][t].q[i]);
-            acc[t] = fmaf((float)p, s * act[u][t].d[i], acc[t]);
+            for (int i = 0; i < NBL; ++i) {
+              uint32_t w[8];
+              bl[u][r].expand(i, cb, w);
+              const float s = bl[u][r].scale(i);
+#pragma unroll
+              for (int t = 0; t < Q; ++t) {
+                const int p = block_dot(w, act[u][t].q[i]);
+                acc[r][t] = fmaf((float)p, s * act[u][t].d[i], acc[r][t]);
+              }
+            }
           }
-        }
       }
     }
   }
 #pragma unroll
-  for (int t = 0; t < Q; ++t) {
-    const float v = group_sum(acc[t], lpr);
-    if (sl == 0 && row_ok) y[(size_t)t * rows + row] = v;
-  }
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < Q; ++t) {
+      const float v = group_sum(acc[r][t], lpr);
+      if (sl == 0 && row_ok[r]) y[(size_t)t * rows + row[r]] = v;
+    }
 }
 
-template <int FMT, int Q, int UF>
+template <int FMT, int Q, int UF, int R>
 __global__ __launch_bounds__(256) void k_matvec(const uint8_t* __restrict__ W, int64_t rows, size_t row_bytes, int nb,
                                                 int lpr_log2, const int8_t* __restrict__ cbp,
                                                 const int8_t* __restrict__ xq, const float* __restrict__ dx,
                                                 float* __restrict__ y) {
-  matvec_body<FMT, Q, UF>(W, rows, row_bytes, nb, lpr_log2, cbp, xq, dx, y);
+  matvec_body<FMT, Q, UF, R>(W, rows, row_bytes, nb, lpr_log2, cbp, xq, dx, y);
 }
 
 // The same matvec with the activation quantization in the launch, when the
@@ -534,15 +554,22 @@ namespace {
 template <int FMT, int Q>
 void launch_matvec_t(const uint8_t* W, int64_t rows, size_t row_bytes, int nb, int lpr_log2, const int8_t* cb,
                      const int8_t* xq, const float* dx, float* y, hipStream_t s) {
-  const int rows_per_wg = 4 * (64 >> lpr_log2);
-  const unsigned grid = (unsigned)((rows + rows_per_wg - 1) / rows_per_wg);
   constexpr int NBL = (FMT == 4) ? 1 : 2;
   const int chunks = (nb + (NBL << lpr_log2) - 1) / (NBL << lpr_log2);
+  // three or four columns over rows of several chunks (one row per wave): two
+  // rows per wave share the activation loads (with one or two columns the
+  // halved workgroup count cost more than the shared loads saved)
+  const int R = (Q >= 3 && chunks > 1 && lpr_log2 == 6) ? 2 : 1;
+  const int rows_per_wg = 4 * R * (64 >> lpr_log2);
+  const unsigned grid = (unsigned)((rows + rows_per_wg - 1) / rows_per_wg);
   if (chunks == 1)
-    launch_kernel("matvec", k_matvec<FMT, Q, 1>, dim3(grid), dim3(256), s, W, rows, row_bytes, nb, lpr_log2, cb, xq,
-                  dx, y);
+    launch_kernel("matvec", k_matvec<FMT, Q, 1, 1>, dim3(grid), dim3(256), s, W, rows, row_bytes, nb, lpr_log2, cb,
+                  xq, dx, y);
+  else if (R == 2)
+    launch_kernel("matvec", k_matvec<FMT, Q, 2, (Q >= 3) ? 2 : 1>, dim3(grid), dim3(256), s, W, rows, row_bytes, nb,
+                  lpr_log2, cb, xq, dx, y);
   else
-    launch_kernel("matvec", k_matvec<FMT, Q, (Q <= 2) ? 4 : 2>, dim3(grid), dim3(256), s, W, rows, row_bytes, nb,
+    launch_kernel("matvec", k_matvec<FMT, Q, (Q <= 2) ? 4 : 2, 1>, dim3(grid), dim3(256), s, W, rows, row_bytes, nb,
                   lpr_log2, cb, xq, dx, y);
 }
 
