@@ -15,7 +15,7 @@
 // Launch sequence (one stream, no host synchronisation):
 //   quant_act   int8 per 32-block of every token (+ H32), shared by all experts
 //   router/topk fp64 logits, top-k, softmax (the decode router's kernels)
-//   k_count     one workgroup per expert: number of pairs routed to it
+//   k_count     one workgroup per expert: number of pairs routed to it (16-byte reads)
 //   k_scan      expert offsets and the tile list (expert, first pair) of 64-pair tiles
 //   k_scatter   one workgroup per expert: its pairs (t*K + s) in ascending order
 //   k_gateup    per (tile, 64 rows): int8 MFMA 16x16x32 per 32-block, so every
@@ -81,11 +81,30 @@ __device__ __forceinline__ int block_sum_256(int v, int* s_red) {
   return r;
 }
 
+// Pair ids are read 16 bytes per lane (when idx is 16-byte aligned, as the
+// workspace places it), kCountBatch pieces per lane in flight at once.
+constexpr int kCountBatch = 8;
+
 __global__ __launch_bounds__(256) void k_count(const int32_t* __restrict__ idx, int npairs, int32_t* counts) {
   __shared__ int s_red[4];
   const int e = blockIdx.x;
+  const uint32_t ue = (uint32_t)e;
   int c = 0;
-  for (int p = threadIdx.x; p < npairs; p += 256) c += (idx[p] == e) ? 1 : 0;
+  const int n4 = ((reinterpret_cast<uintptr_t>(idx) & 15u) == 0) ? npairs / 4 : 0;
+  const u32x4* v4 = reinterpret_cast<const u32x4*>(idx);
+  for (int q0 = threadIdx.x; q0 < n4; q0 += 256 * kCountBatch) {
+    u32x4 v[kCountBatch];
+#pragma unroll
+    for (int k = 0; k < kCountBatch; ++k) v[k] = v4[min(q0 + 256 * k, n4 - 1)];
+    // an empty asm taking every piece keeps all the loads ahead of their uses
+    asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
+#pragma unroll
+    for (int k = 0; k < kCountBatch; ++k) {
+      const int n = (v[k].x == ue) + (v[k].y == ue) + (v[k].z == ue) + (v[k].w == ue);
+      c += (q0 + 256 * k < n4) ? n : 0;
+    }
+  }
+  for (int p = 4 * n4 + threadIdx.x; p < npairs; p += 256) c += (idx[p] == e) ? 1 : 0;
   c = block_sum_256(c, s_red);
   if (threadIdx.x == 0) counts[e] = c;
 }
@@ -120,14 +139,47 @@ __global__ __launch_bounds__(512) void k_scan(const int32_t* __restrict__ counts
   }
 }
 
-// Workgroup e writes the pairs routed to expert e in ascending order.
+// Workgroup e writes the pairs routed to expert e in ascending order. With a
+// 16-byte aligned idx, each pass covers 1024 pairs: lane tid holds pairs
+// 4q..4q+3 (q = pass base + tid), and a workgroup-wide exclusive scan of the
+// lanes' match counts, in lane order, places them; the last npairs % 4 pairs
+// (and an unaligned idx) take passes of 256 pairs with one pair per lane.
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx, int npairs,
                                                  const int32_t* __restrict__ offsets, int32_t* pairs) {
   __shared__ int s_w[4];
   const int e = blockIdx.x;
+  const uint32_t ue = (uint32_t)e;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int pos = offsets[e];
-  for (int p0 = 0; p0 < npairs; p0 += 256) {
+  const int n4 = ((reinterpret_cast<uintptr_t>(idx) & 15u) == 0) ? npairs / 4 : 0;
+  const u32x4* v4 = reinterpret_cast<const u32x4*>(idx);
+  for (int q0 = 0; q0 < n4; q0 += 256) {
+    const int q = q0 + (int)threadIdx.x;
+    const u32x4 v = v4[min(q, n4 - 1)];
+    const bool ok = q < n4;
+    const bool m0 = ok && v.x == ue, m1 = ok && v.y == ue, m2 = ok && v.z == ue, m3 = ok && v.w == ue;
+    const int cnt = (int)m0 + (int)m1 + (int)m2 + (int)m3;
+    int incl = cnt;   // inclusive scan over the wave's lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (lane == 63) s_w[wave] = incl;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) before += (w < wave) ? s_w[w] : 0;
+    const int total = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+    int at = pos + before + incl - cnt;
+    if (m0) pairs[at++] = 4 * q;
+    if (m1) pairs[at++] = 4 * q + 1;
+    if (m2) pairs[at++] = 4 * q + 2;
+    if (m3) pairs[at] = 4 * q + 3;
+    pos += total;
+    __syncthreads();
+  }
+  for (int p0 = 4 * n4; p0 < npairs; p0 += 256) {
     const int p = p0 + threadIdx.x;
     const bool m = p < npairs && idx[p] == e;
     const uint64_t b = __ballot(m);
