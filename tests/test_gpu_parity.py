@@ -80,9 +80,13 @@ def test_block_dots_bit_exact(fmt, rows, k):
 # ------------------------------------------------------------------ matvec
 
 @pytest.mark.parametrize("fmt,rows,k,rot", [(2, 512, 256, 0), (2, 300, 768, 1), (3, 129, 2048, 1),
-                                            (3, 64, 256, 0), (4, 100, 1024, 0), (4, 70, 16384, 1)])
-@pytest.mark.parametrize("ncols", [1, 2, 4])
+                                            (3, 64, 256, 0), (4, 100, 1024, 0), (4, 70, 16384, 1),
+                                            (2, 37, 512, 1), (3, 75, 16384, 0)])
+@pytest.mark.parametrize("ncols", [1, 2, 3, 4])
 def test_matvec(fmt, rows, k, rot, ncols):
+    """Both launch forms (activation quantization inside the matvec when the
+    columns hold at most 64 blocks, a separate launch otherwise), one and two
+    rows per wave (three or four columns over long rows), ragged row counts."""
     c = gen.matvec_case(fmt, rows, k, ncols=ncols, seed=30, rot=rot)
     y_ref, xq_ref, d_ref = dots.matvec(fmt, c.codes, c.scales, c.cb, c.x, rot)
     m = qm.device.DeviceMatrix(c)

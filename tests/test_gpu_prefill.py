@@ -56,6 +56,33 @@ def test_prefill_tiny_ragged(ntok):
     assert np.array_equal(idx, idx_ref)
 
 
+@pytest.mark.parametrize("ntok,topk", [(1, 2), (7, 3), (333, 6), (1030, 5)])
+def test_prefill_grouping_exact(ntok, topk):
+    """Expert grouping for pair counts that are and are not multiples of four
+    (the grouping reads pair ids 16 bytes at a time and takes the last
+    npairs % 4 one by one) and that span several 1024-pair passes: counts
+    equal the histogram of the routing ids, offsets their exclusive scan, and
+    each expert's pairs are exactly its pair indices in ascending order."""
+    spec = gen.LayerSpec.tiny(n_experts=24, topk=topk)
+    dl = qm.device.DeviceLayer(spec, seed=44)
+    x = gen.tokens(ntok, spec.hidden, seed=44)
+    xd = qm.device.to_device(x)
+    out = torch.empty_like(xd)
+    ws = dl.workspace(ntok)
+    qm.qmoe_prefill_layer(dl.desc, xd, out, ws)
+    torch.cuda.synchronize()
+    lay = qm.qmoe_workspace_layout(dl.desc, ntok)
+    E, K = spec.n_experts, spec.topk
+    idx = ws[lay["idx"]: lay["idx"] + 4 * ntok * K].cpu().numpy().view(np.int32).reshape(ntok, K)
+    grp = ws[lay["group"]: lay["group"] + 4 * (3 * E + 1 + ntok * K)].cpu().numpy().view(np.int32)
+    counts, offsets, pairs = grp[:E], grp[E:2 * E + 1], grp[3 * E + 1:]
+    flat = idx.ravel()
+    assert np.array_equal(counts, np.bincount(flat, minlength=E))
+    assert offsets[0] == 0 and offsets[E] == ntok * K and np.array_equal(np.diff(offsets), counts)
+    for e in range(E):
+        assert np.array_equal(pairs[offsets[e]: offsets[e + 1]], np.flatnonzero(flat == e))
+
+
 @pytest.mark.parametrize("rots", [(0, 1), (1, 0), (1, 1)])
 def test_prefill_rotations(rots):
     spec = gen.LayerSpec.tiny(rot_gateup=rots[0], rot_down=rots[1])
