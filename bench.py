@@ -120,7 +120,8 @@ def main():
         print(json.dumps({"prefill_8k": res}), flush=True)
         return
     if args.quantize_only:
-        print(json.dumps({"quantize_fp2": bench_quantize(torch, qm, gen, dev)}), flush=True)
+        print(json.dumps({"quantize_fp2": bench_quantize(torch, qm, gen, dev),
+                          "quantize_fp3": bench_quantize(torch, qm, gen, dev, fmt=3, rows=4096, k=2048)}), flush=True)
         return
     ws = dl.workspace(4)
     toks = torch.from_numpy(gen.tokens(64, spec.hidden, seed=0, stream=7)).to(dev)
@@ -411,6 +412,7 @@ def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
 
     # ---------------------------------------------------------------- weight quantizer
     res["quantize_fp2"] = bench_quantize(torch, qm, gen, dev)
+    res["quantize_fp3"] = bench_quantize(torch, qm, gen, dev, fmt=3, rows=4096, k=2048)
 
     # ---------------------------------------------------------------- FP2 512x256 matvec latency
     c = gen.fp2_matvec(0)
@@ -427,28 +429,30 @@ def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
     return res
 
 
-def bench_quantize(torch, qm, gen, dev, n=16, rows=2048, k=4096, iters=8):
-    """qmoe_quantize on the gate and up matrices of 8 experts (n = 16 fp32
-    2048 x 4096 matrices, N(0, 0.02) with 0.1% outliers), FP2, 8 Lloyd
-    iterations. Algorithmic HBM bytes per weight: norm 4 (fp32 in) + 2 (int16
-    out) + 1/16 (scale); assign 2 per iteration; pack 2 + 1/16 in, 10/32 out."""
+def bench_quantize(torch, qm, gen, dev, fmt=2, n=16, rows=2048, k=4096, iters=8):
+    """qmoe_quantize of n fp32 matrices (N(0, 0.02) with 0.1% outliers), 8 Lloyd
+    iterations: FP2 on the gate and up matrices of 8 experts (16 x 2048 x 4096),
+    FP3 on the down matrices of 16 experts (16 x 4096 x 2048). Algorithmic HBM
+    bytes per weight: norm 4 (fp32 in) + 2 (int16 out) + 1/16 (scale); assign 2
+    per iteration; pack 2 + 1/16 in, block bytes / 32 out."""
+    bb = {2: 10, 3: 14, 4: 17}[fmt]
     w = torch.from_numpy(gen.float_matrices(n, rows, k, seed=0)).to(dev)
-    out = torch.empty((n, rows, (k // 32) * 10), dtype=torch.uint8, device=dev)
-    cb = torch.empty((n, 4), dtype=torch.int8, device=dev)
+    out = torch.empty((n, rows, (k // 32) * bb), dtype=torch.uint8, device=dev)
+    cb = torch.empty((n, 1 << fmt), dtype=torch.int8, device=dev)
     ws = torch.empty(qm.qmoe_quantize_workspace_bytes(n, rows, k), dtype=torch.uint8, device=dev)
-    qm.qmoe_quantize(2, w, iters, out, cb, ws)
+    qm.qmoe_quantize(fmt, w, iters, out, cb, ws)
     torch.cuda.synchronize()
     reps = 5
     with Timer(torch) as t:
         for _ in range(reps):
-            qm.qmoe_quantize(2, w, iters, out, cb, ws)
+            qm.qmoe_quantize(fmt, w, iters, out, cb, ws)
     ms = t.ms / reps
     qm.qmoe_timing_enable(True)
     for _ in range(reps):
-        qm.qmoe_quantize(2, w, iters, out, cb, ws)
+        qm.qmoe_quantize(fmt, w, iters, out, cb, ws)
     torch.cuda.synchronize()
     nw = n * rows * k
-    per_w = {"qz_norm": 4 + 2 + 2 / 32, "qz_assign": 2.0, "qz_pack": 2 + 2 / 32 + 10 / 32}
+    per_w = {"qz_norm": 4 + 2 + 2 / 32, "qz_assign": 2.0, "qz_pack": 2 + 2 / 32 + bb / 32}
     kern = {}
     for name in ("qz_norm", "qz_assign", "qz_update", "qz_pack"):
         avg, _ = kernel_avg_ms(qm, name)
@@ -462,7 +466,7 @@ def bench_quantize(torch, qm, gen, dev, n=16, rows=2048, k=4096, iters=8):
     res = {"ms_per_call": round(ms, 3), "matrices": n, "shape": [rows, k], "iters": iters,
            "weights_per_s": round(nw / (ms * 1e-3), 1), "fp32_input_GBps": round(4 * nw / (ms * 1e-3) / 1e9, 1),
            "kernels": kern}
-    log(f"quantize FP2 {n}x{rows}x{k}, {iters} iters: {ms:.3f} ms; kernels: {kern}")
+    log(f"quantize FP{fmt} {n}x{rows}x{k}, {iters} iters: {ms:.3f} ms; kernels: {kern}")
     del w, out, ws
     return res
 

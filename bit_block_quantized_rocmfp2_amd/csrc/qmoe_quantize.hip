@@ -286,7 +286,7 @@ __global__ __launch_bounds__(256) void k_qz_assign(const int16_t* __restrict__ v
   const u32x4* src = reinterpret_cast<const u32x4*>(v + (size_t)m * per_mat);
   const size_t npieces = per_mat / 8;   // 8 values per 16-byte piece
   const size_t first = (size_t)blockIdx.x * 256 + tid, stride = (size_t)G * 256;
-  if (inc && NC == 4)
+  if (inc && NC <= 8)
     qz_assign_sorted_pairs<NC>(src, npieces, first, stride, mid, s_sum, s_cnt);
   else if (inc)
     qz_assign_loop<NC, true>(src, npieces, first, stride, cc, mid, s_sum, s_cnt);
