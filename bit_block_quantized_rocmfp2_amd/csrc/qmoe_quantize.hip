@@ -20,7 +20,7 @@
 //                starting centroids.
 //   k_qz_assign  one Lloyd assignment pass: G workgroups per matrix stream its
 //                v, each lane keeps per-entry sums and counts in LDS slots of
-//                its own (no contention; with 4 sorted entries, in registers
+//                its own (no contention; with 4 or 8 sorted entries, in registers
 //                as sums above each threshold, from packed int16 arithmetic),
 //                and each workgroup writes its integer partial sums; no
 //                global atomics.
@@ -365,15 +365,37 @@ __global__ __launch_bounds__(256) void k_qz_pack(const int16_t* __restrict__ v, 
 #pragma unroll
     for (int i = 0; i < NC; ++i) cb[(size_t)m * NC + i] = (int8_t)C[i];
   }
+  // with strictly increasing int8 entries the nearest one is the count of
+  // pairwise sums below 2x (qz_nearest_sorted, the same index as the scan);
+  // entries that rounded to equal values take the full scan (ties go low)
+  int mid[NC - 1];
+  bool inc = true;
+#pragma unroll
+  for (int i = 0; i < NC - 1; ++i) {
+    mid[i] = cc[i] + cc[i + 1];
+    inc = inc && cc[i] < cc[i + 1];
+  }
   const u32x4* src = reinterpret_cast<const u32x4*>(v + blk * 32);
+  u32x4 pc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) pc[q] = src[q];
   uint32_t code[32];
+  if (inc) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const u32x4 p = src[q];
-    const uint32_t wd[4] = {p.x, p.y, p.z, p.w};
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t wd[4] = {pc[q].x, pc[q].y, pc[q].z, pc[q].w};
 #pragma unroll
-    for (int h = 0; h < 8; ++h)
-      code[8 * q + h] = (uint32_t)qz_nearest<NC>((int)(int16_t)(wd[h >> 1] >> (16 * (h & 1))), cc);
+      for (int h = 0; h < 8; ++h)
+        code[8 * q + h] = (uint32_t)qz_nearest_sorted<NC>((int)(int16_t)(wd[h >> 1] >> (16 * (h & 1))), mid);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t wd[4] = {pc[q].x, pc[q].y, pc[q].z, pc[q].w};
+#pragma unroll
+      for (int h = 0; h < 8; ++h)
+        code[8 * q + h] = (uint32_t)qz_nearest<NC>((int)(int16_t)(wd[h >> 1] >> (16 * (h & 1))), cc);
+    }
   }
   uint8_t* row = out + (size_t)m * rows * row_bytes + (size_t)r * row_bytes;
   if constexpr (FMT == 2 || FMT == 3) {
