@@ -141,6 +141,17 @@ def main():
     bytes_q1 = spec.topk * per_expert
     value = bytes_q1 / (ms * 1e-3) / 1e9
     log(f"decode q=1: {ms * 1e3:.2f} us/call, {value:.1f} GB/s effective")
+    # per-call distribution: a pair of events around each of K back-to-back calls
+    evk = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        evk[i][0].record()
+        decode_q1(i)
+        evk[i][1].record()
+    torch.cuda.synchronize()
+    per_call = np.array([a.elapsed_time(b) for a, b in evk]) * 1e3
+    pct = {f"p{p}": round(float(np.percentile(per_call, p)), 2) for p in (10, 50, 90)}
+    log(f"decode q=1 per-call events (us): {pct}")
 
     # cold-cache variant: before each call a 512 MiB device write (not timed)
     # evicts the 256 MB last-level cache and the L2s, then the call alone is
@@ -215,23 +226,17 @@ def main():
                 "kernel": "k_gateup1<2> (6 experts x gate+up FP2 = 31,457,280 algorithmic bytes per launch)"}
     down_gbs = spec.topk * down_bytes / (kern["down"] * 1e-3) / 1e9
 
-    # measured HBM stream reference (STREAM "copy" convention): a 1 GiB
-    # device-to-device copy, bytes read + bytes written over its time
-    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    with Timer(torch) as tr:
-        for _ in range(10):
-            dst.copy_(src)
-    read_gbs = 2 * (1 << 30) / (tr.ms / 10 * 1e-3) / 1e9
-    del src, dst
-    log(f"HBM stream reference (1 GiB device copy, read + write bytes): {read_gbs:.1f} GB/s")
+    # measured HBM read peak: the library's read-only streaming probe over 1 GiB
+    # (the best of several grid sizes); a 1 GiB device copy is kept beside it
+    probes = bench_probes(torch, qm, dev)
+    read_gbs = probes["stream_read"]["peak_GBps"]
     router_bytes = spec.n_experts * spec.hidden * 2
     roofline["measured_stream_peak"] = round(read_gbs, 1)
+    roofline["measured_stream_peak_kind"] = "read-only stream, 1 GiB (qmoe_probe_read)"
     roofline["frac_of_measured_stream_peak"] = round(achieved / read_gbs, 4)
 
     extra = {"decode_q1": {"us_per_call": round(ms * 1e3, 2), "tokens_per_s": round(1.0 / (ms * 1e-3), 1),
+                           "us_per_call_events": pct,
                            "effective_GBps_with_router": round((bytes_q1 + router_bytes) / (ms * 1e-3) / 1e9, 1),
                            "frac_of_measured_stream_peak": round(value / read_gbs, 4),
                            "effective_GBps": round(value, 1), "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
@@ -241,14 +246,21 @@ def main():
                            "single_call_after_512MiB_read_us": round(ms_cold_r * 1e3, 2),
                            "single_call_warm_us": round(ms_single * 1e3, 2),
                            "graph_replay_us_per_call": round(ms_graph * 1e3, 2),
-                           "graph_replay_GBps": round(bytes_q1 / (ms_graph * 1e-3) / 1e9, 1)}}
+                           "graph_replay_GBps": round(bytes_q1 / (ms_graph * 1e-3) / 1e9, 1)},
+             "probes": probes}
 
     if not args.no_extra:
         extra.update(bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev))
+        pf = extra.get("prefill_8k", {})
+        if pf.get("gemm_int8_TOPS"):
+            mf = probes["mfma_int8"]
+            pf["gemm_frac_of_measured_mfma_16x16x32"] = round(pf["gemm_int8_TOPS"] / mf["k16x16x32_TOPS"], 4)
+            pf["gemm_frac_of_valu_epilogue_ceiling"] = round(pf["gemm_int8_TOPS"] / probes["valu_epilogue"]
+                                                             ["int8_TOPS_ceiling"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, spec, dl, per_expert)
+        cpu = cpu_baseline(args, spec, dl, per_expert, extra)
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
@@ -429,6 +441,99 @@ def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
     return res
 
 
+def bench_probes(torch, qm, dev):
+    """Measured denominators from the library's probe kernels (qmoe_probe_*):
+    the sustained read-only HBM rate, the cost of one cold streaming launch of B
+    bytes (fitted as latency + B / rate), the int8 matrix-core rate alone (both
+    MFMA forms) and the vector-ALU rate of the prefill GEMMs' per-block epilogue
+    (convert + fused multiply-add), which bounds those GEMMs at
+    64 int8 ops per epilogue element-block."""
+    res = {}
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    n = 1 << 30
+    buf = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    best, per_grid = 0.0, {}
+    for grid in (cu, 2 * cu, 4 * cu, 8 * cu, 16 * cu):
+        for _ in range(2):
+            qm.qmoe_probe_read(buf, grid, sink)
+        with Timer(torch) as t:
+            for _ in range(10):
+                qm.qmoe_probe_read(buf, grid, sink)
+        gbs = 10 * n / (t.ms * 1e-3) / 1e9
+        per_grid[str(grid)] = round(gbs, 1)
+        best = max(best, gbs)
+    # the same over a 1 GiB device copy (bytes read + written), for reference
+    dst = torch.empty_like(buf)
+    dst.copy_(buf)
+    with Timer(torch) as t:
+        for _ in range(10):
+            dst.copy_(buf)
+    copy_gbs = 2 * 10 * n / (t.ms * 1e-3) / 1e9
+    del dst
+    res["stream_read"] = {"peak_GBps": round(best, 1), "bytes": n, "GBps_by_grid": per_grid,
+                          "frac_hbm_peak": round(best / HBM_PEAK_GBS, 4),
+                          "device_copy_read_plus_write_GBps": round(copy_gbs, 1)}
+    log(f"probe: read-only stream {best:.1f} GB/s (by grid {per_grid}); 1 GiB copy {copy_gbs:.1f} GB/s")
+
+    # one cold launch per size: a 512 MiB read of another buffer first evicts the
+    # last-level cache (clean lines), then one probe launch reads B bytes at a
+    # fresh offset; the kernel's own time from in-dispatch events
+    flush = torch.ones((512 << 20) // 4, dtype=torch.int32, device=dev)
+    sizes = [2097152, 5242880, 22020096, 31457280, 53477376, 134217728]
+    pts = []
+    for B in sizes:
+        ts = []
+        for rep in range(6):
+            off = ((rep * 7 + 3) * (64 << 20)) % (n - B) // 256 * 64   # int32 elements, 256-byte aligned
+            view = buf[off: off + B // 4]
+            qm.qmoe_probe_read(flush, 0, sink)
+            qm.qmoe_timing_enable(True)
+            qm.qmoe_probe_read(view, 0, sink)
+            torch.cuda.synchronize()
+            ms, cnt = qm.qmoe_timing_read("probe_read")
+            qm.qmoe_timing_enable(False)
+            ts.append(ms / cnt)
+        pts.append((B, float(np.median(ts))))
+    del flush
+    A = np.array([[1.0, b] for b, _ in pts])
+    y = np.array([t for _, t in pts]) * 1e-3
+    (lat, inv_bw), *_ = np.linalg.lstsq(A, y, rcond=None)
+    res["cold_launch_read"] = {"us_by_bytes": {str(b): round(t * 1e3, 2) for b, t in pts},
+                               "fit_latency_us": round(lat * 1e6, 2), "fit_GBps": round(1.0 / inv_bw / 1e9, 1),
+                               "grid": 4 * cu}
+    log(f"probe: one cold read launch = {lat * 1e6:.2f} us + B / {1.0 / inv_bw / 1e9:.1f} GB/s "
+        f"({ {b: round(t * 1e3, 2) for b, t in pts} } us)")
+
+    # int8 matrix cores alone, and the epilogue's vector-ALU rate
+    grid = 4 * cu
+    sink2 = torch.empty(grid * 256, dtype=torch.int32, device=dev)
+    mf = {}
+    for kind, name, mnk in ((0, "k16x16x32", 16 * 16 * 32), (1, "k32x32x32", 32 * 32 * 32)):
+        iters = 256
+        qm.qmoe_probe_mfma(kind, iters, grid, sink2)
+        with Timer(torch) as t:
+            for _ in range(5):
+                qm.qmoe_probe_mfma(kind, iters, grid, sink2)
+        ops = 5 * grid * 4 * iters * 4 * 2 * mnk
+        mf[f"{name}_TOPS"] = round(ops / (t.ms * 1e-3) / 1e12, 1)
+    mf["frac_spec_peak_k16x16x32"] = round(mf["k16x16x32_TOPS"] / INT8_MFMA_PEAK_TOPS, 4)
+    mf["frac_spec_peak_k32x32x32"] = round(mf["k32x32x32_TOPS"] / INT8_MFMA_PEAK_TOPS, 4)
+    res["mfma_int8"] = mf
+    iters = 8192
+    qm.qmoe_probe_valu(iters, grid, sink2)
+    with Timer(torch) as t:
+        for _ in range(5):
+            qm.qmoe_probe_valu(iters, grid, sink2)
+    eb = 5 * grid * 256 * iters * 16 / (t.ms * 1e-3)
+    res["valu_epilogue"] = {"element_blocks_per_s": round(eb, 1),
+                            "fp32_vector_TFLOPs": round(eb * 2 * 2 / 1e12, 1),   # convert + FMA (2 flops)
+                            "int8_TOPS_ceiling": round(eb * 64 / 1e12, 1)}
+    log(f"probe: int8 MFMA {mf}; epilogue {eb:.3e} element-blocks/s -> ceiling {eb * 64 / 1e12:.1f} TOPS")
+    del buf, sink, sink2
+    return res
+
+
 def bench_quantize(torch, qm, gen, dev, fmt=2, n=16, rows=2048, k=4096, iters=8):
     """qmoe_quantize of n fp32 matrices (N(0, 0.02) with 0.1% outliers), 8 Lloyd
     iterations: FP2 on the gate and up matrices of 8 experts (16 x 2048 x 4096),
@@ -511,31 +616,105 @@ def bench_prefill(torch, qm, gen, spec, dl, dev):
             "gemm_frac_int8_mfma_peak": round(gemm_tops / INT8_MFMA_PEAK_TOPS, 4) if gemm_tops else None}
 
 
-def cpu_baseline(args, spec, dl, per_expert):
-    """The oracle (numpy, fp64) on a bounded sample: a few q=1 decode tokens."""
-    from oracle import moe, router
+def oracle_threads():
+    """Host threads for the oracle: the process's CPU affinity, at most 16 (one
+    GPU's share of the host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _pmap(fn, items, n):
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(n) as ex:
+        return list(ex.map(fn, items))
+
+
+def cpu_baseline(args, spec, dl, per_expert, extra):
+    """The oracle (numpy, fp64; never tuned) timed on bounded samples of the
+    benchmark's workloads. Tokens (and the columns of a dense call) are
+    independent, so the multi-threaded legs hand whole tokens to a thread pool
+    of the affinity core count; numpy's array arithmetic releases the
+    interpreter lock. Input generation is not timed. The headline leg (q=1
+    decode, the same layer and tokens as the GPU headline) is the returned
+    baseline; the others go to extra["cpu_oracle"]."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import dots, moe, router
     from synth import gen
 
+    nt = oracle_threads()
     n = args.cpu_sample_tokens
-    x = gen.tokens(64, spec.hidden, seed=0, stream=7)[:n]
-    idx, _, _ = router.route(dl.w_router_host, x, None, spec.topk)
     cache = {}
-    for e in np.unique(idx):                       # input generation, not timed
-        for name in ("gate", "up", "down"):
-            t = gen.expert_tensor(spec, name, int(e), 0)
-            cache[(name, int(e))] = (t.fmt, t.codes, t.scales, t.cb)
-    L = moe.Layer(spec.hidden, spec.inter, spec.n_experts, spec.topk, dl.w_router_host,
-                  lambda nm, e: cache[(nm, e)])
-    from threadpoolctl import threadpool_limits
-    with threadpool_limits(limits=1):   # the stated core count: one thread, BLAS included
-        t0 = time.perf_counter()
-        moe.moe_tokens(L, x)
-        dt = time.perf_counter() - t0
+
+    def get(name, e):
+        if (name, e) not in cache:
+            t = gen.expert_tensor(spec, name, e, 0)
+            cache[(name, e)] = (t.fmt, t.codes, t.scales, t.cb)
+        return cache[(name, e)]
+
+    def prepare(L, xs):
+        idx, _, _ = router.route(L.w_router, xs, L.bias, spec.topk)
+        _pmap(lambda ne: get(*ne), sorted({(nm, int(e)) for e in np.unique(idx) for nm in ("gate", "up", "down")}), nt)
+
+    def run_tokens(L, xs, threads):
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            if threads == 1:
+                moe.moe_tokens(L, xs)
+            else:
+                _pmap(lambda t: moe.moe_tokens(L, xs[t:t + 1]), range(xs.shape[0]), threads)
+            return time.perf_counter() - t0
+
+    legs = {}
+    # q = 1 decode: the headline layer and its rotating tokens
+    L = moe.Layer(spec.hidden, spec.inter, spec.n_experts, spec.topk, dl.w_router_host, get)
+    x = gen.tokens(64, spec.hidden, seed=0, stream=7)[:n]
+    prepare(L, x)
+    dt = run_tokens(L, x, nt)
+    dt1 = run_tokens(L, x[: max(1, n // 4)], 1)
     gbs = n * spec.topk * per_expert / dt / 1e9
-    log(f"cpu oracle: {n} tokens in {dt:.1f}s -> {gbs:.4f} GB/s effective")
-    return {"value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} q=1 decode tokens of the same layer (routing + 6 experts each), {dt:.1f} s; "
-                      f"numpy element-wise int64/fp64, single thread"}
+    gbs1 = max(1, n // 4) * spec.topk * per_expert / dt1 / 1e9
+    legs["decode_q1"] = {"GBps": round(gbs, 5), "threads": nt, "tokens": n, "s": round(dt, 2),
+                         "single_thread_GBps": round(gbs1, 5), "single_thread_tokens": max(1, n // 4),
+                         "single_thread_s": round(dt1, 2)}
+    log(f"cpu oracle: decode q=1 {n} tokens on {nt} threads {dt:.1f}s ({gbs:.4f} GB/s); "
+        f"{max(1, n // 4)} tokens on 1 thread {dt1:.1f}s ({gbs1:.4f} GB/s)")
+    # q = 4 decode: two forced-overlap groups (each token independent)
+    groups = [gen.q4_group(spec.hidden, seed=0, variant=v) for v in range(2)]
+    xg = np.concatenate(groups)
+    prepare(L, xg)
+    dt = run_tokens(L, xg, nt)
+    legs["decode_q4"] = {"tokens_per_s": round(xg.shape[0] / dt, 3), "threads": nt, "groups": len(groups),
+                         "s": round(dt, 2)}
+    # 8K prefill: a sample of the Zipf-biased batch's tokens through the per-token oracle
+    bias = gen.zipf_bias(spec.n_experts)
+    Lb = moe.Layer(spec.hidden, spec.inter, spec.n_experts, spec.topk, dl.w_router_host, get, bias)
+    xp = gen.tokens(8192, spec.hidden, seed=0, stream=9)[::256]
+    prepare(Lb, xp)
+    dt = run_tokens(Lb, xp, nt)
+    legs["prefill_8k_sample"] = {"tokens_per_s": round(xp.shape[0] / dt, 3), "threads": nt,
+                                 "sample": f"{xp.shape[0]} of the 8192 tokens (every 256th), per-token oracle",
+                                 "s": round(dt, 2)}
+    cache.clear()
+    # dense mix q = 1 and q = 4: the oracle matvec, one column per thread
+    for ncols in (1, 4):
+        mats = gen.dense_mix(ncols, seed=0)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            for c in mats:
+                _pmap(lambda j: dots.matvec(c.fmt, c.codes, c.scales, c.cb, c.x[j:j + 1], c.rot), range(ncols),
+                      min(nt, ncols))
+            dt = time.perf_counter() - t0
+        nbytes = sum(c.rows * (c.k // 32) * {2: 10, 3: 14, 4: 17}[c.fmt] for c in mats)
+        legs[f"dense_mix_q{ncols}"] = {"GBps": round(nbytes / dt / 1e9, 5), "threads": min(nt, ncols),
+                                       "s": round(dt, 2)}
+        del mats
+    log("cpu oracle legs: " + json.dumps(legs))
+    extra["cpu_oracle"] = legs
+    h = legs["decode_q1"]
+    return {"value": h["GBps"], "unit": "GB/s", "cores": nt, "kind": "oracle",
+            "sample": f"{n} q=1 decode tokens of the same layer (routing + 6 experts each) on a pool of {nt} "
+                      f"threads, {h['s']} s; numpy int64/fp64; single thread: {h['single_thread_GBps']} GB/s "
+                      f"on {h['single_thread_tokens']} tokens"}
 
 
 if __name__ == "__main__":

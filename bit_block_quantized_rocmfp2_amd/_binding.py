@@ -44,7 +44,7 @@ class qmoe_layer(ctypes.Structure):
 
 class qmoe_ws_layout(ctypes.Structure):
     _fields_ = [(n, c_size_t) for n in
-                ("ctrl", "xq", "dx", "idx", "gw", "logits", "plan", "hq", "dh", "group", "ypair", "total")]
+                ("xq", "dx", "idx", "gw", "logits", "plan", "hq", "dh", "group", "ypair", "total")]
 
 
 def _load():
@@ -84,6 +84,11 @@ def _load():
         "qmoe_quant_act": (c_int, [c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
         "qmoe_block_dots": (c_int, [c_int, c_int64, c_int64, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p,
                                     c_void_p]),
+        "qmoe_block_dots_mfma": (c_int, [c_int, c_int64, c_int64, c_void_p, c_size_t, c_void_p, c_void_p, c_int32,
+                                         c_void_p, c_void_p]),
+        "qmoe_probe_read": (c_int, [c_void_p, c_size_t, c_int32, c_void_p, c_void_p]),
+        "qmoe_probe_mfma": (c_int, [c_int32, c_int32, c_int32, c_void_p, c_void_p]),
+        "qmoe_probe_valu": (c_int, [c_int32, c_int32, c_void_p, c_void_p]),
         "qmoe_quantize_workspace_bytes": (c_size_t, [c_int32, c_int64, c_int64]),
         "qmoe_quantize": (c_int, [c_int, c_int32, c_int64, c_int64, c_void_p, c_int32, c_void_p, c_size_t, c_void_p,
                                   c_void_p, c_size_t, c_void_p]),
@@ -103,7 +108,9 @@ EXPORTED = (
     "qmoe_strerror", "qmoe_last_error", "qmoe_version", "qmoe_block_bytes", "qmoe_packed_bytes", "qmoe_pack",
     "qmoe_unpack", "qmoe_layer_check", "qmoe_workspace_bytes", "qmoe_workspace_layout", "qmoe_route",
     "qmoe_decode_layer", "qmoe_prefill_layer", "qmoe_matvec_workspace_bytes", "qmoe_matvec", "qmoe_quant_act",
-    "qmoe_block_dots", "qmoe_matvec_expanded_workspace_bytes", "qmoe_matvec_expanded", "qmoe_quantize_workspace_bytes", "qmoe_quantize", "qmoe_timing_enable", "qmoe_timing_read",
+    "qmoe_block_dots", "qmoe_block_dots_mfma", "qmoe_matvec_expanded_workspace_bytes", "qmoe_matvec_expanded",
+    "qmoe_quantize_workspace_bytes", "qmoe_quantize", "qmoe_timing_enable", "qmoe_timing_read", "qmoe_probe_read",
+    "qmoe_probe_mfma", "qmoe_probe_valu",
 )
 
 
@@ -242,6 +249,24 @@ def qmoe_quant_act(x, rot, xq, dx, stream=None) -> None:
 def qmoe_block_dots(fmt, rows, k, w, cb, xq, P, stream=None) -> None:
     _check(LIB.qmoe_block_dots(fmt, rows, k, _ptr(w), _nbytes(w), _ptr(cb), _ptr(xq), _ptr(P), _stream(stream)),
            "qmoe_block_dots")
+
+
+def qmoe_block_dots_mfma(fmt, rows, k, w, cb, xq, P, stream=None) -> None:
+    """xq: int8 [ncols, k]; P: int32 [ncols, rows, k/32]."""
+    _check(LIB.qmoe_block_dots_mfma(fmt, rows, k, _ptr(w), _nbytes(w), _ptr(cb), _ptr(xq), xq.shape[0], _ptr(P),
+                                    _stream(stream)), "qmoe_block_dots_mfma")
+
+
+def qmoe_probe_read(buf, grid, sink, stream=None) -> None:
+    _check(LIB.qmoe_probe_read(_ptr(buf), _nbytes(buf), grid, _ptr(sink), _stream(stream)), "qmoe_probe_read")
+
+
+def qmoe_probe_mfma(kind, iters, grid, sink, stream=None) -> None:
+    _check(LIB.qmoe_probe_mfma(kind, iters, grid, _ptr(sink), _stream(stream)), "qmoe_probe_mfma")
+
+
+def qmoe_probe_valu(iters, grid, sink, stream=None) -> None:
+    _check(LIB.qmoe_probe_valu(iters, grid, _ptr(sink), _stream(stream)), "qmoe_probe_valu")
 
 
 def qmoe_quantize_workspace_bytes(n: int, rows: int, k: int) -> int:

@@ -31,6 +31,8 @@ int check_tensor(const char* name, int fmt, int64_t rows, int64_t k, int64_t E,
   const size_t need = (size_t)E * rows * row_bytes;
   if (w_bytes < need) QMOE_FAIL(QMOE_E_SIZE, "%s: %zu weight bytes < %zu required", name, w_bytes, need);
   if (!cb) QMOE_FAIL(QMOE_E_CODEBOOK, "%s: missing codebook (NULL)", name);
+  // the kernels read each expert's 4, 8 or 16 entries as whole dwords
+  if (reinterpret_cast<uintptr_t>(cb) % 4) QMOE_FAIL(QMOE_E_INVAL, "%s: codebook not 4-byte aligned", name);
   const size_t cb_need = (size_t)E << fi.bits;
   if (cb_bytes < cb_need)
     QMOE_FAIL(QMOE_E_CODEBOOK, "%s: truncated codebook: %zu bytes < %lld experts x %d entries", name, cb_bytes,
@@ -58,6 +60,9 @@ extern "C" int qmoe_layer_check(const qmoe_layer* L) {
   if (L->hidden % 32 || L->inter % 32) QMOE_FAIL(QMOE_E_SHAPE, "hidden=%d / inter=%d not multiples of 32", L->hidden, L->inter);
   if (L->hidden > kMaxHidden) QMOE_FAIL(QMOE_E_SHAPE, "hidden=%d exceeds %d", L->hidden, kMaxHidden);
   if (!L->w_router) QMOE_FAIL(QMOE_E_INVAL, "router: missing weights (NULL)");
+  // router rows are read in 16-byte pieces (64 B per 32-block), the bias as fp64
+  if (reinterpret_cast<uintptr_t>(L->w_router) % 16) QMOE_FAIL(QMOE_E_INVAL, "router: weights not 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(L->router_bias) % 8) QMOE_FAIL(QMOE_E_INVAL, "router: bias not 8-byte aligned");
   const size_t rneed = (size_t)L->n_experts * L->hidden * 2;
   if (L->w_router_bytes < rneed) QMOE_FAIL(QMOE_E_SIZE, "router: %zu bytes < %zu required", L->w_router_bytes, rneed);
   int st;
@@ -86,7 +91,6 @@ extern "C" int qmoe_workspace_layout(const qmoe_layer* L, int32_t max_tokens, qm
     off = round_up(off + bytes, kAlign);
     return at;
   };
-  o->ctrl = take(4096);
   o->xq = take(T * H);
   o->dx = take(T * (H / 32) * 4);
   o->idx = take(T * K * 4);

@@ -63,7 +63,6 @@ struct DecodeArgs {
   const int8_t* cb_down;
   const float* x;
   float* out;
-  uint32_t* ctrl;
   int8_t* xq;
   float* dx;
   double* logits;
@@ -941,7 +940,6 @@ extern "C" int qmoe_decode_layer(const qmoe_layer* L, const float* x, int32_t q,
   a.cb_down = L->cb_down;
   a.x = x;
   a.out = out;
-  a.ctrl = w.ctrl;
   a.xq = w.xq;
   a.dx = w.dx;
   a.logits = w.logits;

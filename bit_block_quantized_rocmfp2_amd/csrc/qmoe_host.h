@@ -9,18 +9,6 @@
 
 namespace qmoe {
 
-// Layer workspace control words (uint32, in the `ctrl` region). Each counter has
-// a 256-byte line of its own so that polling one does not queue behind traffic
-// to another.
-enum CtrlWord : int {
-  kCtrlError = 0,          // sticky device error flags (bit 0: a bounded wait timed out)
-  kCtrlTicket = 64,        // next task ticket of the persistent decode kernel
-  kCtrlRouterDone = 128,   // router tasks finished
-  kCtrlPlanReady = 192,    // top-k and expert plan published
-  kCtrlGateUpDone = 256,   // gate/up tasks finished
-  kCtrlExit = 320,         // workgroups that left the task loop
-};
-
 // Decode plan (int32 words in the `plan` region): [0] U distinct experts,
 // [1..32] expert ids ascending, [33..64] column masks, fp32 weights from word
 // 128: w[u][t] for u < 32, t < 4.
@@ -50,7 +38,6 @@ inline int lanes_per_row(int nb, int nbl) {
 }
 
 struct WsPtrs {
-  uint32_t* ctrl;
   int8_t* xq;
   float* dx;
   int32_t* idx;
@@ -84,6 +71,10 @@ void launch_kernel(const char* name, F kernel, dim3 grid, dim3 block, hipStream_
 
 // Number of compute units of the current device, cached.
 int device_cu_count();
+
+// Host checks of one packed matrix and its codebook (format, shape, NULL,
+// alignment, size); fills *fi.
+int check_matrix(int fmt, int64_t rows, int64_t k, const void* w, size_t w_bytes, const int8_t* cb, FormatInfo* fi);
 
 // Launch helpers shared by the entry points (qmoe_kernels.hip).
 int launch_quant(const float* x, int64_t nblocks, int rot, int8_t* xq, float* dx, hipStream_t s);

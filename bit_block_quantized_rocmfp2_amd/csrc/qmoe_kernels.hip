@@ -503,7 +503,6 @@ int ws_ptrs(const qmoe_layer* L, int32_t ntok, void* ws, size_t ws_bytes, WsPtrs
   if (ws_bytes < lay.total)
     QMOE_FAIL(QMOE_E_WORKSPACE, "workspace %zu bytes < %zu required for %d tokens", ws_bytes, lay.total, ntok);
   uint8_t* b = static_cast<uint8_t*>(ws);
-  p->ctrl = reinterpret_cast<uint32_t*>(b + lay.ctrl);
   p->xq = reinterpret_cast<int8_t*>(b + lay.xq);
   p->dx = reinterpret_cast<float*>(b + lay.dx);
   p->idx = reinterpret_cast<int32_t*>(b + lay.idx);
@@ -610,6 +609,10 @@ void launch_matvec_f(int q, const uint8_t* W, int64_t rows, size_t row_bytes, in
   }
 }
 
+}  // namespace
+
+namespace qmoe {
+
 int check_matrix(int fmt, int64_t rows, int64_t k, const void* w, size_t w_bytes, const int8_t* cb, FormatInfo* fi) {
   if (!format_info(fmt, fi)) QMOE_FAIL(QMOE_E_FORMAT, "unknown format %d", fmt);
   if (rows < 0 || k <= 0 || k % 32)
@@ -628,7 +631,7 @@ int check_matrix(int fmt, int64_t rows, int64_t k, const void* w, size_t w_bytes
   return QMOE_OK;
 }
 
-}  // namespace
+}  // namespace qmoe
 
 extern "C" int qmoe_quant_act(const float* x, int64_t n_vec, int64_t k, int32_t rot, int8_t* xq, float* dx,
                               void* stream) {

@@ -249,7 +249,7 @@ struct StageLds {
 // tensors `wm[]`) and of the activation rows `arow[j]` into registers, then
 // stores them to LDS. Thread layout: 256 threads; each weight row's KB blocks of
 // code bytes (KB*LW*4 bytes) are read as 16-byte pieces.
-template <int FMT, int NMAT>
+template <int FMT, int NMAT, bool SCALES = true>
 struct StageLoader {
   static constexpr int LW = Fmt<FMT>::kLoWords;
   static constexpr int CW = kKB * LW / 4;            // u32x4 per row of code words (4 or 8)
@@ -262,6 +262,8 @@ struct StageLoader {
 
   // arow: int8 activation row of pair tid >> 2; adrow: scale row of pair tid >> 1
   // w0, w1: the weight matrices (w1 is used when NMAT == 2)
+  // (SCALES = false: the weight and activation scales are neither loaded nor
+  // stored, and adrow is not read)
   __device__ __forceinline__ void load(const uint8_t* w0, const uint8_t* w1, size_t row_bytes, int nb, int row0,
                                        int b0, const int8_t* arow, const float* adrow) {
     const int tid = threadIdx.x;
@@ -283,7 +285,7 @@ struct StageLoader {
                           (size_t)b0 * 4;
       hiw = reinterpret_cast<const u32x4*>(hp)[c];
     }
-    {
+    if constexpr (SCALES) {
       const size_t sc_off = (size_t)nb * (LW * 4 + 4 * Fmt<FMT>::kHi);
       const int id = tid % (NMAT * kTileM);
       const int m = id / kTileM, r = id % kTileM;
@@ -301,7 +303,7 @@ struct StageLoader {
       const u32x4* src = reinterpret_cast<const u32x4*>(arow + (size_t)b0 * 32) + 4 * c;
 #pragma unroll
       for (int i = 0; i < 4; ++i) act[i] = src[i];
-      adx = reinterpret_cast<const u32x4*>(adrow + b0)[tid & 1];
+      if constexpr (SCALES) adx = reinterpret_cast<const u32x4*>(adrow + b0)[tid & 1];
     }
   }
 
@@ -320,7 +322,7 @@ struct StageLoader {
         *reinterpret_cast<u32x4*>(&S.h[m][r][4 * c]) = hiw;
       }
     }
-    if (tid < NMAT * kTileM) {
+    if (SCALES && tid < NMAT * kTileM) {
       const int m = tid / kTileM, r = tid % kTileM;
       const uint32_t v[4] = {sc.x, sc.y, sc.z, sc.w};
 #pragma unroll
@@ -337,7 +339,7 @@ struct StageLoader {
       const int j = tid >> 2, c = tid & 3;
 #pragma unroll
       for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&S.x[j][16 * c + 4 * i]) = act[i];
-      if (tid < 2 * kTileN) {
+      if (SCALES && tid < 2 * kTileN) {
         const int jj = tid >> 1, cc = tid & 1;
         S.dx[4 * cc + 0][jj] = __uint_as_float(adx.x);
         S.dx[4 * cc + 1][jj] = __uint_as_float(adx.y);
@@ -348,19 +350,16 @@ struct StageLoader {
   }
 };
 
-// Multiply one stage: wave w owns rows 16w..16w+15 of each matrix and the
-// tile's pairs as up to four 16-column MFMA tiles (nn of them hold pairs). acc[m][n][r] accumulates row 16w + 4q + r,
-// column 16n + l % 16 (q = l / 16), in fp32: per block, the int32 MFMA result
-// times (weight scale x activation scale).
-// The scale products of one block form a 64-column x 16-row outer product per
-// matrix; one fp32 4-block MFMA (K = 1, one rounding per product, as a plain
-// fp32 multiply) leaves product (16n + l % 16, row 16w + 4q + r) in register
-// 4n + r of lane l, the same place as the int32 result it scales, which takes
-// the multiply off the vector ALU: per element and block only the convert and
-// the fused multiply-add remain.
-template <int FMT, int NMAT>
-__device__ __forceinline__ void stage_mma(const StageLds<FMT, NMAT>& S, const uint32_t cb[NMAT][4],
-                                          float acc[NMAT][4][4], int nn) {
+// The int8 products of one stage: wave w owns rows 16w..16w+15 of each matrix
+// and the tile's pairs as up to four 16-column MFMA tiles (nn of them hold
+// pairs). Per 32-block b, hook(b) runs once, then for each subtile n < nn and
+// matrix m one v_mfma_i32_16x16x32_i8 gives the block's exact int32 sums and
+// use(b, m, n, P) consumes them: P[r] in lane l is row 16w + 4q + r, column
+// 16n + l % 16 (q = l / 16). Both the GEMMs and the block-sum test entry point
+// go through this function.
+template <int FMT, int NMAT, typename Hook, typename Use>
+__device__ __forceinline__ void stage_int8(const StageLds<FMT, NMAT>& S, const uint32_t cb[NMAT][4], int nn,
+                                           Hook&& hook, Use&& use) {
   constexpr int LW = Fmt<FMT>::kLoWords;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i16 = lane & 15, q = lane >> 4;
@@ -371,25 +370,44 @@ __device__ __forceinline__ void stage_mma(const StageLds<FMT, NMAT>& S, const ui
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
       A[m] = expand_a<FMT>(&S.w[m][ra][b * LW], Fmt<FMT>::kHi ? S.h[m][Fmt<FMT>::kHi ? ra : 0][b] : 0u, q, cb[m]);
-    const float dl = S.dx[b][lane];        // activation scale of column `lane`
-    v16f p[NMAT];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-      p[m] = __builtin_amdgcn_mfma_f32_16x16x1f32(S.s[m][b][ra], dl, v16f{}, 0, 0, 0);
+    hook(b);
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       if (n < nn) {   // 16-column subtiles beyond the tile's pairs are skipped (uniform)
-      const int col = 16 * n + i16;
-      const long B = *reinterpret_cast<const long*>(&S.x[col][b * 8 + 2 * q]);
+        const int col = 16 * n + i16;
+        const long B = *reinterpret_cast<const long*>(&S.x[col][b * 8 + 2 * q]);
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) {
-        const v4i P = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[m], B, v4i{0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[m][n][r] = fmaf((float)P[r], p[m][4 * n + r], acc[m][n][r]);
-      }
+        for (int m = 0; m < NMAT; ++m) use(b, m, n, __builtin_amdgcn_mfma_i32_16x16x32_i8(A[m], B, v4i{0, 0, 0, 0}, 0, 0, 0));
       }
     }
   }
+}
+
+// Multiply one stage into fp32 accumulators: acc[m][n][r] (row 16w + 4q + r,
+// column 16n + l % 16) += float(P) x (weight scale x activation scale).
+// The scale products of one block form a 64-column x 16-row outer product per
+// matrix; one fp32 4-block MFMA (K = 1, one rounding per product, as a plain
+// fp32 multiply) leaves product (16n + l % 16, row 16w + 4q + r) in register
+// 4n + r of lane l, the same place as the int32 result it scales, which takes
+// the multiply off the vector ALU: per element and block only the convert and
+// the fused multiply-add remain.
+template <int FMT, int NMAT>
+__device__ __forceinline__ void stage_mma(const StageLds<FMT, NMAT>& S, const uint32_t cb[NMAT][4],
+                                          float acc[NMAT][4][4], int nn) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ra = 16 * wave + (lane & 15);
+  v16f p[NMAT];
+  stage_int8<FMT, NMAT>(
+      S, cb, nn,
+      [&](int b) {
+        const float dl = S.dx[b][lane];    // activation scale of column `lane`
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) p[m] = __builtin_amdgcn_mfma_f32_16x16x1f32(S.s[m][b][ra], dl, v16f{}, 0, 0, 0);
+      },
+      [&](int, int m, int n, const v4i& P) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[m][n][r] = fmaf((float)P[r], p[m][4 * n + r], acc[m][n][r]);
+      });
 }
 
 struct PrefillArgs {
@@ -604,6 +622,48 @@ int launch_gemms(const PrefillArgs& a, int tiles_max, int ntok, float* out, hipS
   return launch_check("combine");
 }
 
+// ------------------------------------------------------------ raw block sums (test entry point)
+// One workgroup per 64 rows x 64 columns: the prefill stage loader and
+// stage_int8 with NMAT = 1, writing every int32 MFMA result to
+// P[col][row][block] instead of scaling it. Columns past ncols repeat the last
+// column in LDS and are not stored.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_block_dots_mfma(const uint8_t* __restrict__ w, size_t row_bytes, int nb,
+                                                         const uint32_t* __restrict__ cbw, const int8_t* __restrict__ xq,
+                                                         int ncols, int32_t* __restrict__ P) {
+  __shared__ StageLds<FMT, 1> S;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int row0 = blockIdx.x * kTileM, col0 = blockIdx.y * kTileN;
+  const int cnt = min(kTileN, ncols - col0);
+  const int nn = (cnt + 15) >> 4;
+  const int8_t* arow = xq + (size_t)min(col0 + (tid >> 2), ncols - 1) * ((size_t)nb * 32);
+  uint32_t cb[1][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) cb[0][i] = (i < Fmt<FMT>::kCbWords) ? cbw[i] : 0u;
+  const int i16 = lane & 15, q = lane >> 4;
+  for (int st = 0; st < nb / kKB; ++st) {
+    {
+      StageLoader<FMT, 1, false> L;
+      L.load(w, w, row_bytes, nb, row0, st * kKB, arow, nullptr);
+      __syncthreads();
+      L.store(S);
+    }
+    __syncthreads();
+    stage_int8<FMT, 1>(
+        S, cb, nn, [](int) {},
+        [&](int b, int, int n, const v4i& R) {
+          const int col = col0 + 16 * n + i16;
+          if (16 * n + i16 < cnt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int row = row0 + 16 * wave + 4 * q + r;
+              P[((size_t)col * gridDim.x * kTileM + row) * nb + st * kKB + b] = R[r];
+            }
+          }
+        });
+  }
+}
+
 template <int FG>
 int launch_gemms_g(const PrefillArgs& a, int fd, int tiles_max, int ntok, float* out, hipStream_t s) {
   if (fd == 2) return launch_gemms<FG, 2>(a, tiles_max, ntok, out, s);
@@ -612,6 +672,35 @@ int launch_gemms_g(const PrefillArgs& a, int fd, int tiles_max, int ntok, float*
 }
 
 }  // namespace
+
+extern "C" int qmoe_block_dots_mfma(int fmt, int64_t rows, int64_t k, const void* w, size_t w_bytes,
+                                    const int8_t* cb, const int8_t* xq, int32_t ncols, int32_t* P, void* stream) {
+  clear_error();
+  FormatInfo fi;
+  int st = check_matrix(fmt, rows, k, w, w_bytes, cb, &fi);
+  if (st) return st;
+  if (ncols < 1 || ncols > kTileN) QMOE_FAIL(QMOE_E_SHAPE, "ncols=%d outside 1..%d", ncols, kTileN);
+  if (rows % kTileM || k % (32 * kKB))
+    QMOE_FAIL(QMOE_E_SHAPE, "rows=%lld must be a multiple of %d and k=%lld of %d", (long long)rows, kTileM,
+              (long long)k, 32 * kKB);
+  if (rows == 0) return QMOE_OK;
+  if ((rows / kTileM) > 0x7FFFFFFF || (size_t)ncols * rows * (k / 32) > ((size_t)1 << 40))
+    QMOE_FAIL(QMOE_E_SHAPE, "rows=%lld too large", (long long)rows);
+  if (!xq || !P) QMOE_FAIL(QMOE_E_INVAL, "NULL pointer");
+  if (!aligned16(xq) || (reinterpret_cast<uintptr_t>(P) & 3)) QMOE_FAIL(QMOE_E_INVAL, "xq not 16-byte / P not 4-byte aligned");
+  const int nb = (int)(k / 32);
+  const size_t row_bytes = (size_t)nb * fi.block_bytes;
+  const dim3 grid((unsigned)(rows / kTileM), 1);
+  hipStream_t s = as_stream(stream);
+  const uint8_t* W = static_cast<const uint8_t*>(w);
+  const uint32_t* cbw = reinterpret_cast<const uint32_t*>(cb);
+  switch (fmt) {
+    case 2: launch_kernel("block_dots_mfma", k_block_dots_mfma<2>, grid, dim3(256), s, W, row_bytes, nb, cbw, xq, (int)ncols, P); break;
+    case 3: launch_kernel("block_dots_mfma", k_block_dots_mfma<3>, grid, dim3(256), s, W, row_bytes, nb, cbw, xq, (int)ncols, P); break;
+    default: launch_kernel("block_dots_mfma", k_block_dots_mfma<4>, grid, dim3(256), s, W, row_bytes, nb, cbw, xq, (int)ncols, P); break;
+  }
+  return launch_check("block_dots_mfma");
+}
 
 extern "C" int qmoe_prefill_layer(const qmoe_layer* L, const float* x, int32_t ntok, float* out, void* ws,
                                   size_t ws_bytes, void* stream) {

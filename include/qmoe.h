@@ -74,18 +74,26 @@ const char* qmoe_last_error(void);
 /* ABI version (major * 100 + minor). */
 int qmoe_version(void);
 
-/* Bytes per 32-weight block: 10, 14, 17; 0 for an unknown format. */
+/* Bytes per 32-weight block: 10, 14, 17; 0 for an unknown format
+ * ([Strix-284B] ROCmFPX section: 2.50 / 3.50 / 4.25 bits per weight). */
 size_t qmoe_block_bytes(int fmt);
 /* rows * (k/32) * block bytes; 0 if k % 32 != 0 or the format is unknown. */
 size_t qmoe_packed_bytes(int fmt, int64_t rows, int64_t k);
 
 /* HOST (CPU only). Packs codes (host uint8 [rows*k], each < 2^bits) and scales
  * (host; uint16 fp16 bits [rows*k/32] for FP2/FP3, uint8 E8M0 [rows*k/32] for
- * FP4) into `out` (host, out_bytes >= qmoe_packed_bytes). Rejects codes out of
- * range (QMOE_E_INVAL), non-finite fp16 or E8M0 0xFF scales (QMOE_E_SCALE). */
+ * FP4) into `out` (host, out_bytes >= qmoe_packed_bytes), in the row-planar
+ * block layout above. The pages fix only the block: 32 weights as packed
+ * low-bit codes plus a small scale in 10, 14 or 17 bytes, with a file layout
+ * designed together with the kernel that reads it ([Strix-284B], ROCmFPX
+ * section); the bit positions are this library's. Rejects codes out of range
+ * (QMOE_E_INVAL), non-finite fp16 or E8M0 0xFF scales (QMOE_E_SCALE), k not a
+ * multiple of 32 (QMOE_E_SHAPE), out_bytes too small (QMOE_E_SIZE). */
 int qmoe_pack(int fmt, int64_t rows, int64_t k, const uint8_t* codes,
               const void* scales, void* out, size_t out_bytes);
-/* HOST. Inverse of qmoe_pack. */
+/* HOST. Inverse of qmoe_pack (same passage): codes (host uint8 [rows*k]) and
+ * scales (host, as for qmoe_pack) from packed rows (host, packed_bytes >=
+ * qmoe_packed_bytes). Errors as qmoe_pack; the scales are not re-validated. */
 int qmoe_unpack(int fmt, int64_t rows, int64_t k, const void* packed,
                 size_t packed_bytes, uint8_t* codes, void* scales);
 
@@ -111,15 +119,25 @@ typedef struct {
   const int8_t* cb_down; size_t cb_down_bytes;
 } qmoe_layer;
 
-/* HOST check of a layer descriptor (no device access): shapes, formats,
- * rotation flags, missing / truncated / mismatched weights and codebooks. */
+/* HOST check of a layer descriptor (no device access), the load-time
+ * validation of [0731-Strix], integration section (codebooks that are missing,
+ * truncated or mismatched are refused before serving starts) and of [evox3],
+ * introduction (a rotation the kernels do not implement must be refused at
+ * load, not at layer 3, expert 7 of a running server). Checks: shapes and
+ * limits (QMOE_E_SHAPE); format and rotation values, gate/up format equality
+ * (QMOE_E_FORMAT); NULL weights, weights or router not 16-byte aligned,
+ * codebooks not 4-byte aligned, bias not 8-byte aligned (QMOE_E_INVAL); weight
+ * or router buffers shorter than their shapes (QMOE_E_SIZE); codebooks NULL
+ * (missing), shorter (truncated) or longer (mismatched) than E * 2^bits bytes
+ * (QMOE_E_CODEBOOK). Each expert's codebook is a separate array slot, so a
+ * duplicated entry cannot arise in this descriptor. */
 int qmoe_layer_check(const qmoe_layer* L);
 
 /* Bytes of device workspace needed by qmoe_route / qmoe_decode_layer /
  * qmoe_prefill_layer for up to `max_tokens` tokens (0 on an invalid layer).
- * The workspace must be zero-filled once before its first use; every call
- * leaves its control words zero again on exit. Calls that share a workspace
- * must be ordered (same stream or synchronised). */
+ * The workspace needs no initialisation: every call writes each region before
+ * it reads it, and its contents are scratch between calls. Calls that share a
+ * workspace must be ordered (same stream or synchronised). */
 size_t qmoe_workspace_bytes(const qmoe_layer* L, int32_t max_tokens);
 
 /* Router only: logits in fp64 in a fixed order (per block sequential, then a
@@ -163,28 +181,53 @@ size_t qmoe_matvec_workspace_bytes(int64_t k, int32_t ncols);
 
 /* Dense block-quantized matvec / small matmul: y[c][r] = sum_b s[r][b] d_c[b] P_c[r][b]
  * for columns c < ncols (1..4), with x quantized per 32-block (rot 0 or 1).
- * w: packed [rows][row_bytes]; cb: int8 [2^bits]; x: fp32 [ncols][k];
- * y: fp32 [ncols][rows]. Each block is expanded once for all columns. */
+ * The packed blocks are read directly and their codebook expanded in registers
+ * for integer dot products ([Strix-284B], ROCmFPX section); up to four columns
+ * share each decoded block, the q = 4 weight reuse of the dense ROCmFP4 path
+ * ([Strix-284B], decode section); rot = 1 is the H32 input rotation of the
+ * fused H32 matvec ([evox3], table "The optimization ladder").
+ * w: packed [rows][row_bytes] (w_bytes >= qmoe_packed_bytes, 16-byte aligned);
+ * cb: int8 [2^bits]; x: fp32 [ncols][k] (16-byte aligned); y: fp32
+ * [ncols][rows]; ws: qmoe_matvec_workspace_bytes(k, ncols) bytes, scratch.
+ * Errors before any launch: QMOE_E_FORMAT (format, rot), QMOE_E_SHAPE (k, rows,
+ * ncols), QMOE_E_INVAL (NULL or misaligned), QMOE_E_SIZE, QMOE_E_WORKSPACE. */
 int qmoe_matvec(int fmt, int64_t rows, int64_t k, const void* w, size_t w_bytes,
                 const int8_t* cb, int32_t rot, const float* x, int32_t ncols,
                 float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* Activation quantization only: x fp32 [n_vec][k] -> xq int8 [n_vec][k],
- * dx fp32 [n_vec][k/32]. */
+ * dx fp32 [n_vec][k/32] (all device). The int8 per-32-block activations that
+ * the integer dot products consume ([Strix-284B], ROCmFPX section), with the
+ * optional H32 rotation of each input block ([evox3], table "The optimization
+ * ladder": H32 support and the shared H32 input); the arithmetic is the one in
+ * the preamble above. Errors: QMOE_E_SHAPE (k % 32), QMOE_E_FORMAT (rot),
+ * QMOE_E_INVAL (NULL). */
 int qmoe_quant_act(const float* x, int64_t n_vec, int64_t k, int32_t rot,
                    int8_t* xq, float* dx, void* stream);
 
 /* Per-block exact integer sums P[r][b] = sum_j C[code] * xq[32b+j] (int32),
- * through the same expansion and dot code as the layer kernels.
- * xq: int8 [k]; P: int32 [rows][k/32]. */
+ * the integer dot product of an expanded block with int8 activations
+ * ([Strix-284B], ROCmFPX section), through the same expansion and sdot4 code
+ * as the decode and matvec kernels. xq: int8 [k]; P: int32 [rows][k/32] (both
+ * device). Errors as qmoe_matvec. */
 int qmoe_block_dots(int fmt, int64_t rows, int64_t k, const void* w, size_t w_bytes,
                     const int8_t* cb, const int8_t* xq, int32_t* P, void* stream);
+
+/* The same per-block sums for ncols (1..64) int8 columns through the prefill
+ * kernels' matrix-core path: the A operand expanded from the packed codes by
+ * byte permutes, one int8 MFMA per 32-block and 16-column subtile, as the
+ * prefill expert GEMMs compute them ([evox3], table "The optimization ladder":
+ * the batched multi-token prefill). xq: int8 [ncols][k]; P: int32
+ * [ncols][rows][k/32] (device). rows: a multiple of 64; k: a multiple of 256.
+ * Errors as qmoe_matvec (ncols outside 1..64: QMOE_E_SHAPE). */
+int qmoe_block_dots_mfma(int fmt, int64_t rows, int64_t k, const void* w, size_t w_bytes,
+                         const int8_t* cb, const int8_t* xq, int32_t ncols, int32_t* P,
+                         void* stream);
 
 /* Byte offsets of the internal buffers inside a layer workspace, so that a caller
  * can inspect intermediate results (int8 activations, routing, SwiGLU outputs).
  * Fields are byte offsets from the workspace start. */
 typedef struct {
-  size_t ctrl;        /* uint32 control words; word 0 = device error flags */
   size_t xq;          /* int8  [max_tokens][hidden]                        */
   size_t dx;          /* fp32  [max_tokens][hidden/32]                     */
   size_t idx;         /* int32 [max_tokens][topk]                          */
@@ -199,6 +242,31 @@ typedef struct {
 } qmoe_ws_layout;
 
 int qmoe_workspace_layout(const qmoe_layer* L, int32_t max_tokens, qmoe_ws_layout* out);
+
+/* Measurement probes: the denominators that the path's kernels are compared
+ * with. They are not steps of the layer; each is asynchronous on `stream` and
+ * allocates nothing.
+ *   qmoe_probe_read: a read-only stream of `bytes` (a multiple of 16) from
+ *     `buf` (device, 16-byte aligned) by `grid` workgroups of 256 threads (0 =
+ *     4 per compute unit), each reading a contiguous share with 16-byte loads
+ *     and writing one word of a checksum to sink[blockIdx] (device, grid
+ *     words), so that no load is dead.
+ *   qmoe_probe_mfma: `iters` rounds of back-to-back int8 MFMAs on registers
+ *     only; `kind` 0 = v_mfma_i32_16x16x32_i8 (the form the prefill GEMMs use),
+ *     1 = v_mfma_i32_32x32x32_i8 (the gfx950 form at the full int8 rate);
+ *     grid workgroups of 256 threads (0 = 4 per compute unit); each lane adds
+ *     its results into sink[global thread id] (device, grid*256 words). The
+ *     int8 ops are grid * 4 waves * iters * 4 MFMAs * 2*M*N*K.
+ *   qmoe_probe_valu: `iters` rounds of the per-block fp32 epilogue of the
+ *     prefill GEMMs (an int32 -> fp32 convert and a fused multiply-add per
+ *     element and block) on 16 independent values per lane, registers only;
+ *     grid and sink as qmoe_probe_mfma. Epilogue element-blocks =
+ *     grid * 256 * iters * 16.
+ * Errors: QMOE_E_INVAL (NULL, misaligned, bytes % 16, kind), QMOE_E_SHAPE
+ * (iters < 1). */
+int qmoe_probe_read(const void* buf, size_t bytes, int32_t grid, uint32_t* sink, void* stream);
+int qmoe_probe_mfma(int32_t kind, int32_t iters, int32_t grid, uint32_t* sink, void* stream);
+int qmoe_probe_valu(int32_t iters, int32_t grid, uint32_t* sink, void* stream);
 
 /* Weight quantizer: n fp32 matrices w [n][rows][k] (device, 16-byte aligned,
  * finite) -> packed ROCmFPX rows out [n][rows][row_bytes] (device) and one int8

@@ -132,7 +132,7 @@ def test_layer_check_ok_and_workspace():
     L, _ = host_layer()
     assert status_of(L) == 0
     lay = qm.qmoe_workspace_layout(L, 4)
-    offs = [lay[k] for k in ("ctrl", "xq", "dx", "idx", "gw", "logits", "plan", "hq", "dh", "group", "ypair")]
+    offs = [lay[k] for k in ("xq", "dx", "idx", "gw", "logits", "plan", "hq", "dh", "group", "ypair")]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay["total"] == qm.qmoe_workspace_bytes(L, 4) > lay["ypair"]
     full = gen.LayerSpec.full()
@@ -150,6 +150,24 @@ def test_layer_check_codebook_classes():
     # an FP3 (8-entry) codebook given for the FP2 gate tensor
     L, b = host_layer(cb_gate=np.zeros(spec.n_experts * 8, np.int8))
     assert status_of(L) == -4 and "mismatched" in B.LIB.qmoe_last_error().decode()
+
+
+def test_layer_check_alignment():
+    """The kernels read router rows in 16-byte pieces, codebooks as dwords and the
+    bias as fp64: misaligned pointers are refused on the host."""
+    L, b = host_layer()
+    assert status_of(L) == 0
+    L.w_router += 8
+    assert status_of(L) == -1 and "router" in B.LIB.qmoe_last_error().decode()
+    L, b = host_layer()
+    L.cb_up += 2
+    assert status_of(L) == -1 and "codebook" in B.LIB.qmoe_last_error().decode()
+    L, b = host_layer()
+    bias = np.zeros(gen.LayerSpec.tiny().n_experts + 1, np.float64)
+    L.router_bias = bias.ctypes.data + 4
+    assert status_of(L) == -1 and "bias" in B.LIB.qmoe_last_error().decode()
+    L.router_bias = bias.ctypes.data
+    assert status_of(L) == 0
 
 
 def test_layer_check_shapes_formats_sizes():
