@@ -73,6 +73,8 @@ def _load():
                                c_void_p]),
         "qmoe_decode_layer": (c_int, [POINTER(qmoe_layer), c_void_p, c_int32, c_void_p, c_void_p, c_size_t,
                                       c_void_p]),
+        "qmoe_decode_noalloc_max_bytes": (c_size_t, []),
+        "qmoe_decode_layer_noalloc": (c_int, [POINTER(qmoe_layer), c_void_p, c_int32, c_void_p, c_void_p]),
         "qmoe_prefill_layer": (c_int, [POINTER(qmoe_layer), c_void_p, c_int32, c_void_p, c_void_p, c_size_t,
                                        c_void_p]),
         "qmoe_matvec_workspace_bytes": (c_size_t, [c_int64, c_int32]),
@@ -107,7 +109,7 @@ LIB = _load()
 EXPORTED = (
     "qmoe_strerror", "qmoe_last_error", "qmoe_version", "qmoe_block_bytes", "qmoe_packed_bytes", "qmoe_pack",
     "qmoe_unpack", "qmoe_layer_check", "qmoe_workspace_bytes", "qmoe_workspace_layout", "qmoe_route",
-    "qmoe_decode_layer", "qmoe_prefill_layer", "qmoe_matvec_workspace_bytes", "qmoe_matvec", "qmoe_quant_act",
+    "qmoe_decode_layer", "qmoe_decode_noalloc_max_bytes", "qmoe_decode_layer_noalloc", "qmoe_prefill_layer", "qmoe_matvec_workspace_bytes", "qmoe_matvec", "qmoe_quant_act",
     "qmoe_block_dots", "qmoe_block_dots_mfma", "qmoe_matvec_expanded_workspace_bytes", "qmoe_matvec_expanded",
     "qmoe_quantize_workspace_bytes", "qmoe_quantize", "qmoe_timing_enable", "qmoe_timing_read", "qmoe_probe_read",
     "qmoe_probe_mfma", "qmoe_probe_valu",
@@ -220,6 +222,11 @@ def qmoe_route(L, x, idx, gate_w, ws, stream=None) -> None:
 def qmoe_decode_layer(L, x, out, ws, stream=None) -> None:
     _check(LIB.qmoe_decode_layer(ctypes.byref(L), _ptr(x), x.shape[0], _ptr(out), _ptr(ws), _nbytes(ws),
                                  _stream(stream)), "qmoe_decode_layer")
+
+
+def qmoe_decode_layer_noalloc(L, x, out, stream=None) -> None:
+    _check(LIB.qmoe_decode_layer_noalloc(ctypes.byref(L), _ptr(x), x.shape[0], _ptr(out), _stream(stream)),
+           "qmoe_decode_layer_noalloc")
 
 
 def qmoe_prefill_layer(L, x, out, ws, stream=None) -> None:

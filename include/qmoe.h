@@ -155,6 +155,22 @@ int qmoe_route(const qmoe_layer* L, const float* x, int32_t ntok, int32_t* idx,
 int qmoe_decode_layer(const qmoe_layer* L, const float* x, int32_t q, float* out,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* Decode for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * computation and kernels as qmoe_decode_layer, but the workspace is a fixed
+ * device array inside the library, qmoe_decode_noalloc_max_bytes() (4 MiB) on
+ * each GPU, held until the process ends; no call allocates or frees anything.
+ * Its device address is looked up once per device (hipGetSymbolAddress, with
+ * that device current). Every call on one GPU shares that GPU's array and
+ * leaves its contents behind (nothing in it needs clearing between calls):
+ * calls that overlap on one GPU (unordered streams, several host threads)
+ * race on it and give undefined results. x, out, q, stream and errors as
+ * qmoe_decode_layer; a layer whose decode workspace at q tokens exceeds the
+ * array is refused before any launch (QMOE_E_WORKSPACE). */
+size_t qmoe_decode_noalloc_max_bytes(void);
+int qmoe_decode_layer_noalloc(const qmoe_layer* L, const float* x, int32_t q, float* out,
+                              void* stream);
+
 /* Prefill: ntok tokens through the layer, grouped by expert on the device
  * ([evox3] ladder: layer-major prefill batching). x: fp32 [ntok][hidden];
  * out: fp32 [ntok][hidden]. Deterministic: per token the expert outputs are
