@@ -31,10 +31,10 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, published (TOPS)
-# HBM bytes per launch of k_gateup1<2> (decode q=1), from rocprofv3 FETCH_SIZE and WRITE_SIZE runs scaled by
-# a 256 MiB device copy (profiles/hbm_traffic_decode_q1_prefill_8k.md). Must be re-measured (or set to None)
-# whenever that kernel changes.
-GATEUP_Q1_TRAFFIC_BYTES = 31810712
+# HBM bytes per launch of the dominant decode q=1 kernel (k_gateup1<2>), from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE runs scaled by a 256 MiB device copy (profiles/hbm_traffic_decode_q1_prefill_8k.md). Must be
+# re-measured (or set to None) whenever that kernel changes.
+DOMINANT_Q1_TRAFFIC_BYTES = 31810712
 
 WORKLOAD = ("MoE decode layer q=1: hidden 4096, 256 routed experts, expert intermediate 2048, router W fp16 "
             "N(0,0.02) with softmax top-6, gate/up ROCmFP2 (4-entry per-expert codebooks), down ROCmFP3 "
@@ -114,7 +114,6 @@ def main():
     per_expert = dl.packed_bytes_per_expert()
     log(f"built full layer ({per_expert * spec.n_experts:,} packed bytes) in {time.time() - t0:.1f}s")
     gateup_bytes = qm.qmoe_packed_bytes(2, spec.inter, spec.hidden) * 2
-    down_bytes = qm.qmoe_packed_bytes(3, spec.hidden, spec.inter)
     if args.prefill_only:
         res = bench_prefill(torch, qm, gen, spec, dl, dev)
         print(json.dumps({"prefill_8k": res}), flush=True)
@@ -209,22 +208,27 @@ def main():
     del graph
 
     # dominant kernel, timed with HIP events on the launch stream over K calls
-    qm.qmoe_timing_enable(True)
-    for i in range(K):
-        decode_q1(i)
-    torch.cuda.synchronize()
-    kern = {}
-    for name in ("route", "gateup", "down"):
-        avg, n = kernel_avg_ms(qm, name)
-        kern[name] = avg
-    qm.qmoe_timing_enable(False)
-    log("decode q=1 kernels (us): " + ", ".join(f"{k}={v * 1e3:.2f}" for k, v in kern.items() if v))
-    gu_ms = kern["gateup"]
-    achieved = spec.topk * gateup_bytes / (gu_ms * 1e-3) / 1e9
+    def kernel_times(names):
+        qm.qmoe_timing_enable(True)
+        for i in range(K):
+            decode_q1(i)
+        torch.cuda.synchronize()
+        kt = {}
+        for name in names:
+            avg, n = kernel_avg_ms(qm, name)
+            if avg:
+                kt[name] = avg
+        qm.qmoe_timing_enable(False)
+        return kt
+    kern = kernel_times(("route", "gateup", "down"))
+    log("decode q=1 kernels (us): " + ", ".join(f"{k}={v * 1e3:.2f}" for k, v in kern.items()))
+    dom_ms, dom_bytes = kern["gateup"], spec.topk * gateup_bytes
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": GATEUP_Q1_TRAFFIC_BYTES,
-                "kernel": "k_gateup1<2> (6 experts x gate+up FP2 = 31,457,280 algorithmic bytes per launch)"}
-    down_gbs = spec.topk * down_bytes / (kern["down"] * 1e-3) / 1e9
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": DOMINANT_Q1_TRAFFIC_BYTES,
+                "kernel": "k_gateup1<2> (6 experts x gate+up FP2 = 31,457,280 algorithmic bytes per launch)",
+                "kernel_us": round(dom_ms * 1e3, 2)}
+    down_gbs = spec.topk * qm.qmoe_packed_bytes(3, spec.hidden, spec.inter) / (kern["down"] * 1e-3) / 1e9
 
     # measured HBM read peak: the library's read-only streaming probe over 1 GiB
     # (the best of several grid sizes); a 1 GiB device copy is kept beside it

@@ -337,18 +337,16 @@ constexpr int log2_exact(int n) { return n <= 1 ? 0 : 1 + log2_exact(n / 2); }
 // 8 waves; wave w owns rows 4w..4w+3 of both gate and up of the workgroup's 32
 // rows. Lanes cover NBL consecutive blocks each.
 // One item: rows rb*32 .. rb*32+31 of expert e's gate and up for plan slot u.
-// SwiGLU of the workgroup's 32 rows (wave w holds rows RPW*w .. RPW*w + RPW-1 as
-// per-lane partial sums) and requantization of the 32-row block (+ H32) for each
-// routed column of slot u.
+
+// SwiGLU of the wave's RPW gate and up rows (per-lane partial sums ag / au for
+// each of the Q columns) into s_a[t][rowoff + r] for the routed columns t: the
+// RPW * Q sums over the wave by transposing butterflies with one lane mapping
+// (lane l ends with the gate and up sums of value k = r * Q + t), and the first
+// lane of each group forms its SwiGLU (all values in one pass of the wave).
 template <int Q, int RPW>
-__device__ __forceinline__ void gateup_epilogue(const DecodeArgs& a, uint32_t mask, int u, int rb,
-                                                const float (&ag)[RPW][Q], const float (&au)[RPW][Q],
-                                                float (&s_a)[4][32]) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // the RPW * Q gate and up row sums over the wave, by transposing butterflies
-  // with one lane mapping: lane l ends with the gate and up sums of value
-  // k = r * Q + t, and the first lane of each group forms its SwiGLU (all values
-  // in one pass of the wave)
+__device__ __forceinline__ void gateup_wave_swiglu(uint32_t mask, const float (&ag)[RPW][Q], const float (&au)[RPW][Q],
+                                                   float (&s_a)[4][32], int rowoff) {
+  const int lane = threadIdx.x & 63;
   constexpr int NV = RPW * Q, NP = pow2_at_least(NV);
   float g[NP], uu[NP];
 #pragma unroll
@@ -362,8 +360,19 @@ __device__ __forceinline__ void gateup_epilogue(const DecodeArgs& a, uint32_t ma
   constexpr int GROUP = 64 >> log2_exact(NP);   // lanes holding the same value
   if ((lane & (GROUP - 1)) == 0 && kg < NV) {
     const int r = kg / Q, t = kg % Q;
-    if (mask >> t & 1) s_a[t][wave * RPW + r] = g[0] / (1.0f + expf(-g[0])) * uu[0];
+    if (mask >> t & 1) s_a[t][rowoff + r] = g[0] / (1.0f + expf(-g[0])) * uu[0];
   }
+}
+
+// SwiGLU of the workgroup's 32 rows (wave w holds rows RPW*w .. RPW*w + RPW-1 as
+// per-lane partial sums) and requantization of the 32-row block (+ H32) for each
+// routed column of slot u.
+template <int Q, int RPW>
+__device__ __forceinline__ void gateup_epilogue(const DecodeArgs& a, uint32_t mask, int u, int rb,
+                                                const float (&ag)[RPW][Q], const float (&au)[RPW][Q],
+                                                float (&s_a)[4][32]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  gateup_wave_swiglu<Q, RPW>(mask, ag, au, s_a, wave * RPW);
   __syncthreads();
   // requantize the 32-row block: half-wave h of wave w takes column 2w + h
   if (wave < (Q + 1) / 2) {
@@ -379,20 +388,20 @@ __device__ __forceinline__ void gateup_epilogue(const DecodeArgs& a, uint32_t ma
   }
 }
 
-template <int FMT, int Q>
-__device__ __forceinline__ void gateup_item(const DecodeArgs& a, int e, uint32_t mask, int u, int rb,
-                                            float (&s_a)[4][32]) {
+// The gate and up rows row0 .. row0+RPW-1 of expert e against the routed
+// columns: per-lane partial sums over the lane's blocks (NBL consecutive
+// blocks per lane and pass).
+template <int FMT, int Q, int RPW>
+__device__ __forceinline__ void gateup_stream(const DecodeArgs& a, int e, uint32_t mask, int row0, float (&ag)[RPW][Q],
+                                              float (&au)[RPW][Q]) {
   constexpr int NBL = (FMT == 4) ? 1 : 2;
-  constexpr int RPW = 4;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row0 = rb * 32 + wave * RPW;
+  const int lane = threadIdx.x & 63;
   const uint8_t* gbase = a.gate + (size_t)e * a.gu_stride;
   const uint8_t* ubase = a.up + (size_t)e * a.gu_stride;
   uint32_t cbg[4], cbu[4];
   load_codebook<FMT>(a.cb_gate + ((size_t)e << FMT), cbg);
   load_codebook<FMT>(a.cb_up + ((size_t)e << FMT), cbu);
   const int nb = a.nb_h;
-  float ag[RPW][Q], au[RPW][Q];
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
@@ -434,6 +443,15 @@ __device__ __forceinline__ void gateup_item(const DecodeArgs& a, int e, uint32_t
         }
     }
   }
+}
+
+template <int FMT, int Q>
+__device__ __forceinline__ void gateup_item(const DecodeArgs& a, int e, uint32_t mask, int u, int rb,
+                                            float (&s_a)[4][32]) {
+  constexpr int RPW = 4;
+  const int wave = threadIdx.x >> 6;
+  float ag[RPW][Q], au[RPW][Q];
+  gateup_stream<FMT, Q, RPW>(a, e, mask, rb * 32 + wave * RPW, ag, au);
   gateup_epilogue<Q, RPW>(a, mask, u, rb, ag, au, s_a);
 }
 
