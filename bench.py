@@ -374,6 +374,12 @@ def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
     log(f"decode q=1 FP2 down: {ms2 * 1e3:.2f} us/call, {gbs2:.1f} GB/s")
     del down2, cb_down2
 
+    # ---------------------------------------------------------------- a stack of distinct layers
+    try:
+        res["decode_q1_layer_stack"] = bench_layer_stack(torch, qm, gen, spec, per_expert, dev)
+    except RuntimeError as e:   # e.g. out of device memory
+        res["decode_q1_layer_stack"] = {"status": f"not run: {e}"}
+
     # ---------------------------------------------------------------- prefill 8K (Zipf)
     try:
         res["prefill_8k"] = bench_prefill(torch, qm, gen, spec, dl, dev)
@@ -536,6 +542,48 @@ def bench_probes(torch, qm, dev):
     log(f"probe: int8 MFMA {mf}; epilogue {eb:.3e} element-blocks/s -> ceiling {eb * 64 / 1e12:.1f} TOPS")
     del buf, sink, sink2
     return res
+
+
+def bench_layer_stack(torch, qm, gen, spec, per_expert, dev, n_layers=8, reps=25):
+    """Decode q=1 through n_layers distinct full-size layers (each its own seeded
+    weights and its own token), all captured in one HIP graph and replayed: the
+    steady state of a model whose layers stream their experts from HBM one after
+    another (nothing is reused across layers: 8 x 2.28 GB of experts)."""
+    layers = [qm.device.DeviceLayer(spec, seed=200 + i) for i in range(n_layers)]
+    xs = [torch.from_numpy(gen.tokens(1, spec.hidden, seed=200 + i, stream=13)).to(dev) for i in range(n_layers)]
+    outs = [torch.empty_like(x) for x in xs]
+    ws = layers[0].workspace(1)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for dl, x, o in zip(layers, xs, outs):
+            qm.qmoe_decode_layer(dl.desc, x, o, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for dl, x, o in zip(layers, xs, outs):
+            qm.qmoe_decode_layer(dl.desc, x, o, ws)
+    for _ in range(3):
+        g.replay()
+    with Timer(torch) as t:
+        for _ in range(reps):
+            g.replay()
+    us_layer = t.ms / (reps * n_layers) * 1e3
+    gbs = spec.topk * per_expert / (us_layer * 1e-6) / 1e9
+    # the same layers called eagerly, back to back
+    with Timer(torch) as te:
+        for _ in range(reps):
+            for dl, x, o in zip(layers, xs, outs):
+                qm.qmoe_decode_layer(dl.desc, x, o, ws)
+    us_eager = te.ms / (reps * n_layers) * 1e3
+    del g, layers
+    torch.cuda.empty_cache()
+    log(f"decode q=1, {n_layers} distinct layers in one graph: {us_layer:.2f} us/layer ({gbs:.1f} GB/s); "
+        f"eager {us_eager:.2f} us/layer")
+    return {"layers": n_layers, "us_per_layer_graph": round(us_layer, 2), "us_per_layer_eager": round(us_eager, 2),
+            "effective_GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "distinct_packed_bytes": n_layers * spec.n_experts * per_expert}
 
 
 def bench_quantize(torch, qm, gen, dev, fmt=2, n=16, rows=2048, k=4096, iters=8):

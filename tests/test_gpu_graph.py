@@ -50,3 +50,69 @@ def test_graph_replay_decode():
             assert np.array_equal(o.cpu().numpy(), ref[i]), (rep, i)
         qm.qmoe_decode_layer(dl.desc, other, other_out, ws)   # eager work on the same workspace
         torch.cuda.synchronize()
+
+
+def test_layer_stack_graph_full_size():
+    """A stack of four distinct full-size layers (hidden 4096, 256 experts, inter
+    2048, top-6; gate/up FP2, down FP3), each with its own seeded weights and its
+    own token, decoded one after another from one HIP graph, as a model's
+    layers stream through decode (each layer's experts are read from HBM,
+    nothing is reused across layers). Every replay equals the eager calls bit
+    for bit, with eager work between replays, and each layer's eager output
+    equals the oracle within the bar."""
+    import concurrent.futures as cf
+
+    from oracle import moe
+
+    spec = gen.LayerSpec.full()
+    seeds = [100, 101, 102, 103]
+    layers = [qm.device.DeviceLayer(spec, seed=s) for s in seeds]
+    xs = [torch.from_numpy(gen.tokens(1, spec.hidden, seed=s, stream=13)).cuda() for s in seeds]
+    outs = [torch.empty_like(x) for x in xs]
+    ws = layers[0].workspace(4)
+    ref = []
+    for dl, x, o in zip(layers, xs, outs):
+        qm.qmoe_decode_layer(dl.desc, x, o, ws)
+        torch.cuda.synchronize()
+        ref.append(o.cpu().numpy().copy())
+
+    def oracle(i):
+        cache = {}
+
+        def get(name, e):
+            if (name, e) not in cache:
+                t = gen.expert_tensor(spec, name, e, seeds[i])
+                cache[(name, e)] = (t.fmt, t.codes, t.scales, t.cb)
+            return cache[(name, e)]
+
+        L = moe.Layer(spec.hidden, spec.inter, spec.n_experts, spec.topk, layers[i].w_router_host, get)
+        return moe.moe_tokens(L, xs[i].cpu().numpy())[0]
+
+    with cf.ThreadPoolExecutor(4) as ex:
+        refs = list(ex.map(oracle, range(4)))
+    for i in range(4):
+        assert moe.rel_l2(ref[i], refs[i]) < 1e-3, i
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for dl, x, o in zip(layers, xs, outs):
+            qm.qmoe_decode_layer(dl.desc, x, o, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for dl, x, o in zip(layers, xs, outs):
+            qm.qmoe_decode_layer(dl.desc, x, o, ws)
+    torch.cuda.synchronize()
+    other = torch.from_numpy(gen.tokens(4, spec.hidden, seed=7, stream=14)).cuda()
+    other_out = torch.empty_like(other)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for i, o in enumerate(outs):
+            assert np.array_equal(o.cpu().numpy(), ref[i]), (rep, i)
+        qm.qmoe_decode_layer(layers[rep].desc, other, other_out, ws)   # eager work between replays
+        torch.cuda.synchronize()
+    del g, layers
