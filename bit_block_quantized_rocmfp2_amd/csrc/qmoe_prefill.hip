@@ -43,7 +43,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kTileN = 64;   // pairs (tokens) per tile
-constexpr int kTileM = 64;   // weight rows per workgroup
+constexpr int kTileM = 128;  // weight rows per matrix and workgroup (4 waves x 32)
 constexpr int kKB = 8;       // 32-blocks per LDS stage (K = 256)
 
 // Group region (int32 words): counts[E], offsets[E+1], ntiles at 2E+1 (one word
@@ -196,74 +196,117 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx
 }
 
 // ------------------------------------------------------------ MFMA tiles
-// One 32-block of a weight row, as the A operand of v_mfma_i32_16x16x32_i8: lane
-// l holds row l % 16 and the 8 weights 8q..8q+7 (q = l / 16), i.e. expanded
-// dwords 2q and 2q+1 of the block (see Blocks::expand for the layout facts).
+// Per 32-block, one v_mfma_i32_32x32x32_i8 gives the exact int32 sums of a
+// 32-row x 32-column tile (one block per instruction, the gfx950 full-rate
+// form), and one v_mfma_f32_32x32x8bf16_1k forms the 32 x 32 scale products
+// s_w(row) x d_x(column) in the same register layout from exact bf16 parts:
+// s_w (an fp16 value, or a power of two) = s_hi + s_lo, d_x (fp32) = d_hi +
+// d_mid + d_lo, every part exact in bf16 and every part product exact in fp32,
+// so the K = 6 sum is the fp32 product up to the final roundings. Per element
+// and block the vector ALU then does one convert and one fused multiply-add.
+// Lane layouts (checked on the GPU): operand lane l holds row (or column) l % 32
+// and the 16 bytes of K half l / 32; result register r of lane l is row
+// 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// Weights 16h..16h+15 of one block of a row (h = K half), expanded through the
+// codebook: dword k = weights 16h+4k..+3 (layout facts as in Blocks::expand).
+// lo: the block's code words, hi: its FP3 bit-2 plane.
 template <int FMT>
-__device__ __forceinline__ long expand_a(const uint32_t* lo, uint32_t hi, int q, const uint32_t cb[4]) {
-  uint32_t a0, a1;
+__device__ __forceinline__ v4i expand_a32(const uint32_t* lo, uint32_t hi, int h, const uint32_t cb[4]) {
+  v4i a;
   if constexpr (FMT == 2 || FMT == 3) {
-    const uint32_t w = lo[q >> 1];
-    const int k0 = (2 * q) & 3;
-    uint32_t s0 = (w >> (2 * k0)) & 0x03030303u, s1 = (w >> (2 * k0 + 2)) & 0x03030303u;
-    if constexpr (FMT == 3) {
-      s0 |= ((hi >> (2 * q)) & 0x01010101u) << 2;
-      s1 |= ((hi >> (2 * q + 1)) & 0x01010101u) << 2;
-    }
-    a0 = perm(cb[1], cb[0], s0);
-    a1 = perm(cb[1], cb[0], s1);
-  } else {
-    const uint32_t w = lo[q];
-    uint32_t r[2];
+    const uint32_t w = lo[0];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t sel = (w >> (4 * h)) & 0x0F0F0F0Fu;
+    for (int k = 0; k < 4; ++k) {
+      uint32_t sel = (w >> (2 * k)) & 0x03030303u;
+      if constexpr (FMT == 3) sel |= ((hi >> (4 * h + k)) & 0x01010101u) << 2;
+      a[k] = (int)perm(cb[1], cb[0], sel);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t sel = (lo[k >> 1] >> (4 * (k & 1))) & 0x0F0F0F0Fu;
       const uint32_t s7 = sel & 0x07070707u;
       const uint32_t x = perm(cb[1], cb[0], s7);
       const uint32_t y = perm(cb[3], cb[2], s7);
       const uint32_t m = ((sel >> 3) & 0x01010101u) * 0xFFu;
-      r[h] = (y & m) | (x & ~m);
+      a[k] = (int)((y & m) | (x & ~m));
     }
-    a0 = r[0];
-    a1 = r[1];
   }
-  return (long)(((uint64_t)a1 << 32) | a0);
+  return a;
 }
 
-// LDS for one stage of a 64-row weight tile (up to two matrices) and a 64-pair
-// activation tile. Row strides are padded by 4 dwords (16-byte aligned rows).
+// Exact bf16 parts (bits in the low 16 of each result word) by truncation: a
+// value with at most 11 significant bits (fp16, or a power of two) is hi + lo;
+// an fp32 value is hi + mid + lo (each difference is exact in fp32).
+__device__ __forceinline__ void bf16_split2(float v, uint32_t& hi, uint32_t& lo) {
+#pragma clang fp contract(off)
+  const uint32_t hb = __float_as_uint(v) & 0xFFFF0000u;
+  const float r = v - __uint_as_float(hb);
+  hi = hb >> 16;
+  lo = __float_as_uint(r) >> 16;
+}
+__device__ __forceinline__ void bf16_split3(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+#pragma clang fp contract(off)
+  const uint32_t hb = __float_as_uint(v) & 0xFFFF0000u;
+  const float r1 = v - __uint_as_float(hb);
+  const uint32_t mb = __float_as_uint(r1) & 0xFFFF0000u;
+  const float r2 = r1 - __uint_as_float(mb);
+  hi = hb >> 16;
+  mid = mb >> 16;
+  lo = __float_as_uint(r2) >> 16;
+}
+
+// LDS of one stage: NMAT matrices of 128 rows x 8 blocks and 64 columns x 8
+// blocks of activations. Code words and FP3 planes are stored block-major with
+// rows innermost, so the 32 rows an operand read touches are consecutive
+// words. Scales are stored as their bf16 parts: s = (s_hi | s_lo << 16) per
+// (block, row), d = (d_hi | d_mid << 16, d_lo) per (block, column); a lane
+// builds its bf16 MFMA operand (4 bf16, K = 4 (l / 32) + j) with byte permutes:
+// half 0 = (s_hi, s_hi, s_hi, s_lo) x (d_hi, d_mid, d_lo, d_hi), half 1 =
+// (s_lo, s_lo, 0, 0) x (d_mid, d_lo, 0, 0): the six part products.
 template <int FMT, int NMAT>
 struct StageLds {
   static constexpr int LW = Fmt<FMT>::kLoWords;
-  static constexpr int WS = kKB * LW + 4;    // code words per row
-  static constexpr int HS = kKB + 4;         // high-plane words per row
-  static constexpr int XS = kKB * 8 + 4;     // activation words per pair
-  uint32_t w[NMAT][kTileM][WS];
-  uint32_t h[NMAT][Fmt<FMT>::kHi ? kTileM : 1][HS];
-  float s[NMAT][kKB][kTileM];                // weight scales, block-major
+  static constexpr int XS = kKB * 8 + 4;     // activation words per column (16-byte pieces, spread over banks)
+  uint32_t w[NMAT][kKB][LW][kTileM];
+  uint32_t h[NMAT][kKB][Fmt<FMT>::kHi ? kTileM : 1];
+  uint32_t s[NMAT][kKB][kTileM];           // weight-scale bf16 parts per (block, row)
   uint32_t x[kTileN][XS];
-  float dx[kKB][kTileN];                     // activation scales, block-major
+  u32x2 d[kKB][kTileN];                     // activation-scale bf16 parts per (block, column)
 };
 
+// The bf16 MFMA operands of K half kh from the stored parts (see StageLds).
+__device__ __forceinline__ v4s scale_operand_w(uint32_t sp, int kh) {
+  const uint32_t w0 = perm(sp, sp, kh ? 0x03020302u : 0x01000100u);   // (s_hi, s_hi) or (s_lo, s_lo)
+  return __builtin_bit_cast(v4s, u32x2{w0, kh ? 0u : sp});             // (.., s_hi, s_lo) or (.., 0, 0)
+}
+__device__ __forceinline__ v4s scale_operand_a(u32x2 dp, int kh) {
+  // half 0: (d_hi, d_mid | d_lo, d_hi); half 1: (d_mid, d_lo | 0, 0)
+  const uint32_t w0 = kh ? perm(dp.x, dp.y, 0x01000706u) : dp.x;
+  const uint32_t w1 = kh ? 0u : perm(dp.x, dp.y, 0x05040100u);
+  return __builtin_bit_cast(v4s, u32x2{w0, w1});
+}
+
 // Loads stage `st` of NMAT weight matrices (rows row0.. of the row-planar
-// tensors `wm[]`) and of the activation rows `arow[j]` into registers, then
-// stores them to LDS. Thread layout: 256 threads; each weight row's KB blocks of
-// code bytes (KB*LW*4 bytes) are read as 16-byte pieces.
+// tensors w0, w1) and of the activation rows (arow: int8 row of column tid >> 2,
+// adrow: scale row of column (tid >> 1) & 63) into registers; store() writes
+// them to LDS. 256 threads; every thread issues every load (indices wrapped into
+// range), so no loaded value is defined conditionally.
 template <int FMT, int NMAT, bool SCALES = true>
 struct StageLoader {
   static constexpr int LW = Fmt<FMT>::kLoWords;
   static constexpr int CW = kKB * LW / 4;            // u32x4 per row of code words (4 or 8)
   static constexpr int NCODE = NMAT * kTileM * CW / 256;   // u32x4 per thread (1..4)
+  static constexpr int NHI = (NMAT * 2 * kTileM + 255) / 256;  // FP3 high-plane pieces per thread
   u32x4 code[NCODE];
-  u32x4 hiw;      // FP3 high planes: 8 words (2 x 16 B) per row, one piece per thread
+  u32x4 hiw[NHI]; // FP3 high planes: 8 words (2 x 16 B) per row
   u32x4 sc;       // scales of one row: fp16 8 x 2 B, or E8M0 8 x 1 B (low half)
-  u32x4 act[4];   // 64 pairs x 256 B: the 64-byte quarter (tid & 3) of pair tid >> 2
-  u32x4 adx;      // 64 pairs x 32 B of activation scales: half (tid & 1) of pair tid >> 1
+  u32x4 act[4];   // 64 columns x 256 B: the 64-byte quarter (tid & 3) of column tid >> 2
+  u32x4 adx;      // 64 columns x 32 B of activation scales: half (tid & 1) of column (tid >> 1) & 63
 
-  // arow: int8 activation row of pair tid >> 2; adrow: scale row of pair tid >> 1
-  // w0, w1: the weight matrices (w1 is used when NMAT == 2)
-  // (SCALES = false: the weight and activation scales are neither loaded nor
-  // stored, and adrow is not read)
   __device__ __forceinline__ void load(const uint8_t* w0, const uint8_t* w1, size_t row_bytes, int nb, int row0,
                                        int b0, const int8_t* arow, const float* adrow) {
     const int tid = threadIdx.x;
@@ -275,15 +318,16 @@ struct StageLoader {
       const uint8_t* wb = (NMAT == 2 && m == 1) ? w1 : w0;
       code[i] = reinterpret_cast<const u32x4*>(wb + (size_t)(row0 + r) * row_bytes + (size_t)b0 * LW * 4)[c];
     }
-    // Every thread issues every load (indices wrapped into range); only the LDS
-    // stores are restricted, so no value is defined conditionally.
     if constexpr (Fmt<FMT>::kHi) {
-      // high planes: 8 words = 32 B per row -> 2 u32x4 per row; NMAT*128 pieces
-      const int id = tid % (NMAT * 128);
-      const int m = id / 128, r = (id % 128) >> 1, c = id & 1;
-      const uint8_t* hp = ((NMAT == 2 && m == 1) ? w1 : w0) + (size_t)(row0 + r) * row_bytes + (size_t)nb * LW * 4 +
-                          (size_t)b0 * 4;
-      hiw = reinterpret_cast<const u32x4*>(hp)[c];
+      // high planes: 8 words = 32 B per row -> 2 u32x4 per row; NMAT*2*kTileM pieces
+#pragma unroll
+      for (int i = 0; i < NHI; ++i) {
+        const int id = (tid + 256 * i) % (NMAT * 2 * kTileM);
+        const int m = id / (2 * kTileM), r = (id % (2 * kTileM)) >> 1, c = id & 1;
+        const uint8_t* hp = ((NMAT == 2 && m == 1) ? w1 : w0) + (size_t)(row0 + r) * row_bytes +
+                            (size_t)nb * LW * 4 + (size_t)b0 * 4;
+        hiw[i] = reinterpret_cast<const u32x4*>(hp)[c];
+      }
     }
     if constexpr (SCALES) {
       const size_t sc_off = (size_t)nb * (LW * 4 + 4 * Fmt<FMT>::kHi);
@@ -299,7 +343,7 @@ struct StageLoader {
       }
     }
     {
-      const int c = tid & 3;   // 64-byte quarter c of the pair's 256 bytes
+      const int c = tid & 3;   // 64-byte quarter c of the column's 256 bytes
       const u32x4* src = reinterpret_cast<const u32x4*>(arow + (size_t)b0 * 32) + 4 * c;
 #pragma unroll
       for (int i = 0; i < 4; ++i) act[i] = src[i];
@@ -314,12 +358,23 @@ struct StageLoader {
       const int id = tid + 256 * i;
       const int m = id / (kTileM * CW), rem = id % (kTileM * CW);
       const int r = rem / CW, c = rem % CW;
-      *reinterpret_cast<u32x4*>(&S.w[m][r][4 * c]) = code[i];
+      const uint32_t v[4] = {code[i].x, code[i].y, code[i].z, code[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int q = 4 * c + k;                    // word q of the row's stage: block q / LW, word q % LW
+        S.w[m][q / LW][q % LW][r] = v[k];
+      }
     }
     if constexpr (Fmt<FMT>::kHi) {
-      if (tid < NMAT * 128) {
-        const int m = tid / 128, r = (tid % 128) >> 1, c = tid & 1;
-        *reinterpret_cast<u32x4*>(&S.h[m][r][4 * c]) = hiw;
+#pragma unroll
+      for (int i = 0; i < NHI; ++i) {
+        const int id = tid + 256 * i;
+        if (id < NMAT * 2 * kTileM) {
+          const int m = id / (2 * kTileM), r = (id % (2 * kTileM)) >> 1, c = id & 1;
+          const uint32_t v[4] = {hiw[i].x, hiw[i].y, hiw[i].z, hiw[i].w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) S.h[m][4 * c + k][r] = v[k];
+        }
       }
     }
     if (SCALES && tid < NMAT * kTileM) {
@@ -332,7 +387,9 @@ struct StageLoader {
           f = half_bits_to_float((v[b >> 1] >> (16 * (b & 1))) & 0xFFFFu);
         else
           f = e8m0_to_float((v[b >> 2] >> (8 * (b & 3))) & 0xFFu);
-        S.s[m][b][r] = f;
+        uint32_t hi, lo;
+        bf16_split2(f, hi, lo);
+        S.s[m][b][r] = hi | (lo << 16);
       }
     }
     {
@@ -341,72 +398,91 @@ struct StageLoader {
       for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&S.x[j][16 * c + 4 * i]) = act[i];
       if (SCALES && tid < 2 * kTileN) {
         const int jj = tid >> 1, cc = tid & 1;
-        S.dx[4 * cc + 0][jj] = __uint_as_float(adx.x);
-        S.dx[4 * cc + 1][jj] = __uint_as_float(adx.y);
-        S.dx[4 * cc + 2][jj] = __uint_as_float(adx.z);
-        S.dx[4 * cc + 3][jj] = __uint_as_float(adx.w);
+        const uint32_t v[4] = {adx.x, adx.y, adx.z, adx.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t hi, mid, lo;
+          bf16_split3(__uint_as_float(v[k]), hi, mid, lo);
+          S.d[4 * cc + k][jj] = u32x2{hi | (mid << 16), lo};
+        }
       }
     }
   }
 };
 
-// The int8 products of one stage: wave w owns rows 16w..16w+15 of each matrix
-// and the tile's pairs as up to four 16-column MFMA tiles (nn of them hold
-// pairs). Per 32-block b, hook(b) runs once, then for each subtile n < nn and
-// matrix m one v_mfma_i32_16x16x32_i8 gives the block's exact int32 sums and
-// use(b, m, n, P) consumes them: P[r] in lane l is row 16w + 4q + r, column
-// 16n + l % 16 (q = l / 16). Both the GEMMs and the block-sum test entry point
-// go through this function.
-template <int FMT, int NMAT, typename Hook, typename Use>
-__device__ __forceinline__ void stage_int8(const StageLds<FMT, NMAT>& S, const uint32_t cb[NMAT][4], int nn,
-                                           Hook&& hook, Use&& use) {
+// The int8 products of one stage: wave w owns rows 32w .. 32w+31 of each
+// matrix and the tile's columns as two 32-column subtiles (the second skipped
+// when it holds no column of the tile: ncol columns hold pairs), so one
+// expanded A operand feeds both. Per 32-block b, hook(b) runs once, then for
+// each matrix m and subtile n one v_mfma_i32_32x32x32_i8 gives the block's
+// exact int32 sums and use(b, m, n, P) consumes them (layout above). Both the
+// GEMMs and the block-sum test entry point go through this function.
+template <int FMT, int NMAT, int NN, typename Hook, typename Use>
+__device__ __forceinline__ void stage_int8_nn(const StageLds<FMT, NMAT>& S, const uint32_t cb[NMAT][4], Hook& hook,
+                                              Use& use) {
   constexpr int LW = Fmt<FMT>::kLoWords;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int i16 = lane & 15, q = lane >> 4;
-  const int ra = 16 * wave + i16;          // A-operand row of this lane
-#pragma unroll 2
+  const int kh = lane >> 5;
+  const int ra = 32 * wave + (lane & 31);   // A-operand row of this lane
+#pragma unroll 1
   for (int b = 0; b < kKB; ++b) {
-    long A[NMAT];
+    v4i B[NN];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-      A[m] = expand_a<FMT>(&S.w[m][ra][b * LW], Fmt<FMT>::kHi ? S.h[m][Fmt<FMT>::kHi ? ra : 0][b] : 0u, q, cb[m]);
-    hook(b);
+    for (int n = 0; n < NN; ++n) B[n] = *reinterpret_cast<const v4i*>(&S.x[32 * n + (lane & 31)][b * 8 + 4 * kh]);
+    hook(b, NN);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      if (n < nn) {   // 16-column subtiles beyond the tile's pairs are skipped (uniform)
-        const int col = 16 * n + i16;
-        const long B = *reinterpret_cast<const long*>(&S.x[col][b * 8 + 2 * q]);
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m) use(b, m, n, __builtin_amdgcn_mfma_i32_16x16x32_i8(A[m], B, v4i{0, 0, 0, 0}, 0, 0, 0));
+    for (int m = 0; m < NMAT; ++m) {
+      uint32_t lo[2];
+      if constexpr (LW == 2) {
+        lo[0] = S.w[m][b][kh][ra];
+        lo[1] = 0u;
+      } else {
+        lo[0] = S.w[m][b][2 * kh][ra];
+        lo[1] = S.w[m][b][2 * kh + 1][ra];
       }
+      const uint32_t hi = Fmt<FMT>::kHi ? S.h[m][b][Fmt<FMT>::kHi ? ra : 0] : 0u;
+      const v4i A = expand_a32<FMT>(lo, hi, kh, cb[m]);
+#pragma unroll
+      for (int n = 0; n < NN; ++n) use(b, m, n, __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B[n], v16i{}, 0, 0, 0));
     }
   }
 }
 
-// Multiply one stage into fp32 accumulators: acc[m][n][r] (row 16w + 4q + r,
-// column 16n + l % 16) += float(P) x (weight scale x activation scale).
-// The scale products of one block form a 64-column x 16-row outer product per
-// matrix; one fp32 4-block MFMA (K = 1, one rounding per product, as a plain
-// fp32 multiply) leaves product (16n + l % 16, row 16w + 4q + r) in register
-// 4n + r of lane l, the same place as the int32 result it scales, which takes
-// the multiply off the vector ALU: per element and block only the convert and
-// the fused multiply-add remain.
+// Dispatches on the number of column subtiles that hold pairs (uniform), so
+// each block's products are straight-line code.
+template <int FMT, int NMAT, typename Hook, typename Use>
+__device__ __forceinline__ void stage_int8(const StageLds<FMT, NMAT>& S, const uint32_t cb[NMAT][4], int ncol,
+                                           Hook&& hook, Use&& use) {
+  if (ncol > 32)
+    stage_int8_nn<FMT, NMAT, 2>(S, cb, hook, use);
+  else
+    stage_int8_nn<FMT, NMAT, 1>(S, cb, hook, use);
+}
+
+// Multiply one stage into fp32 accumulators: acc[m][n][r] (row 32w + 8 (r / 4)
+// + 4 (l / 32) + r % 4, column 32n + l % 32) += float(P) x (weight scale x
+// activation scale), each 32 x 32 tile of scale products formed by the bf16
+// MFMA right where it is consumed (its operands are read once per block).
 template <int FMT, int NMAT>
 __device__ __forceinline__ void stage_mma(const StageLds<FMT, NMAT>& S, const uint32_t cb[NMAT][4],
-                                          float acc[NMAT][4][4], int nn) {
+                                          float acc[NMAT][2][16], int ncol) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int ra = 16 * wave + (lane & 15);
-  v16f p[NMAT];
+  const int kh = lane >> 5;
+  const int ra = 32 * wave + (lane & 31);
+  v4s sop[NMAT], dop[2];
   stage_int8<FMT, NMAT>(
-      S, cb, nn,
-      [&](int b) {
-        const float dl = S.dx[b][lane];    // activation scale of column `lane`
+      S, cb, ncol,
+      [&](int b, int nn) {
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) p[m] = __builtin_amdgcn_mfma_f32_16x16x1f32(S.s[m][b][ra], dl, v16f{}, 0, 0, 0);
+        for (int n = 0; n < 2; ++n)
+          if (n < nn) dop[n] = scale_operand_a(S.d[b][32 * n + (lane & 31)], kh);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) sop[m] = scale_operand_w(S.s[m][b][ra], kh);
       },
-      [&](int, int m, int n, const v4i& P) {
+      [&](int, int m, int n, const v16i& P) {
+        const v16f pr = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(sop[m], dop[n], v16f{}, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[m][n][r] = fmaf((float)P[r], p[m][4 * n + r], acc[m][n][r]);
+        for (int r = 0; r < 16; ++r) acc[m][n][r] = fmaf((float)P[r], pr[r], acc[m][n][r]);
       });
 }
 
@@ -452,71 +528,89 @@ __device__ __forceinline__ bool tile_info(const PrefillArgs& a, TileInfo& t) {
   return true;
 }
 
+// Stage loop shared by the GEMMs: each stage is loaded, stored to LDS and
+// multiplied; the other workgroups of the compute unit overlap one another's
+// loads. (Requesting stage st + 1 into registers during the products of stage st
+// was measured slower: the registers it holds cost occupancy.)
+template <int FMT, int NMAT, typename Load, typename Mul>
+__device__ __forceinline__ void stage_loop(StageLds<FMT, NMAT>& S, int nst, Load&& load, Mul&& mul) {
+  for (int st = 0; st < nst; ++st) {
+    StageLoader<FMT, NMAT> L;
+    load(L, st);
+    __syncthreads();               // the previous stage's LDS reads are done
+    L.store(S);
+    __syncthreads();
+    mul();
+  }
+}
+
 // ------------------------------------------------------------ k_gateup
+// A workgroup multiplies 128 rows of gate and of up with one tile of up to 64
+// pairs; wave w owns rows 32w..32w+31 of both matrices and all the tile's
+// columns, so SwiGLU pairs gate and up element by element in registers.
 template <int FMT>
-__global__ __launch_bounds__(256) void k_gateup(PrefillArgs a) {
+struct GateupLds {
+  union {
+    StageLds<FMT, 2> stage;
+    float sa[kTileN][kTileM + 4];      // SwiGLU values [pair][row] for the requantization
+  };
+  int pair[kTileN];
+};
+
+template <int FMT>
+__global__ __launch_bounds__(256, FMT == 4 ? 2 : 3) void k_gateup(PrefillArgs a) {
   TileInfo T;
   if (!tile_info(a, T)) return;
-  __shared__ StageLds<FMT, 2> S;
-  __shared__ int s_pair[kTileN];
+  __shared__ GateupLds<FMT> G;
+  StageLds<FMT, 2>& S = G.stage;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row0 = blockIdx.x * kTileM;
-  const int nn = (T.cnt + 15) >> 4;   // 16-column subtiles holding pairs
-  if (tid < kTileN) s_pair[tid] = a.pairs[T.pbase + min(tid, T.cnt - 1)];   // padding repeats a valid pair
+  if (tid < kTileN) G.pair[tid] = a.pairs[T.pbase + min(tid, T.cnt - 1)];   // padding repeats a valid pair
   __syncthreads();
-  // the token rows this thread loads (pair tid >> 2 for bytes, tid >> 1 for scales)
-  const int8_t* arow = a.xq + (size_t)(s_pair[tid >> 2] / a.K) * a.hidden;
-  const float* adrow = a.dx + (size_t)(s_pair[(tid >> 1) & (kTileN - 1)] / a.K) * a.nb_h;
+  // the token rows this thread loads (column tid >> 2 for bytes, (tid >> 1) & 63 for scales)
+  const int8_t* arow = a.xq + (size_t)(G.pair[tid >> 2] / a.K) * a.hidden;
+  const float* adrow = a.dx + (size_t)(G.pair[(tid >> 1) & (kTileN - 1)] / a.K) * a.nb_h;
   const uint8_t* wg = a.gate + (size_t)T.e * a.gu_stride;
   const uint8_t* wu = a.up + (size_t)T.e * a.gu_stride;
   uint32_t cb[2][4];
   load_codebook<FMT>(a.cb_gate + ((size_t)T.e << FMT), cb[0]);
   load_codebook<FMT>(a.cb_up + ((size_t)T.e << FMT), cb[1]);
-  float acc[2][4][4];
+  float acc[2][2][16];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[m][n][r] = 0.0f;
-  // two weight matrices leave no registers for a prefetch at four waves per SIMD:
-  // each stage is loaded, stored to LDS and multiplied (other workgroups overlap)
-  const int nst = a.nb_h / kKB;
-  for (int st = 0; st < nst; ++st) {
-    {
-      StageLoader<FMT, 2> L;
-      L.load(wg, wu, a.gu_row_bytes, a.nb_h, row0, st * kKB, arow, adrow);
-      __syncthreads();               // the previous stage's LDS reads are done
-      L.store(S);
-    }
-    __syncthreads();
-    stage_mma<FMT, 2>(S, cb, acc, nn);
-  }
-  // SwiGLU into LDS as [pair][row] (reusing the activation stage buffer), then
-  // requantize each (pair, 32-row block).
+      for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
+  stage_loop<FMT, 2>(
+      S, a.nb_h / kKB,
+      [&](StageLoader<FMT, 2>& L, int st) { L.load(wg, wu, a.gu_row_bytes, a.nb_h, row0, st * kKB, arow, adrow); },
+      [&]() { stage_mma<FMT, 2>(S, cb, acc, T.cnt); });
+  // SwiGLU into LDS as [pair][row], then requantize each (pair, 32-row block)
   __syncthreads();
-  float* sa = reinterpret_cast<float*>(&S.x[0][0]);   // 64 x 68 floats fit in x (64 x 68 words)
-  constexpr int AS = StageLds<FMT, 2>::XS;
-  {
-    const int i16 = lane & 15, q = lane >> 4;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      float4 v;
-      float* pv = reinterpret_cast<float*>(&v);
+  for (int n = 0; n < 2; ++n)
+    if (32 * n < T.cnt) {
+      const int col = 32 * n + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float g = acc[0][n][r], u = acc[1][n][r];
-        pv[r] = g / (1.0f + expf(-g)) * u;
+      for (int q = 0; q < 4; ++q) {
+        float4 v;
+        float* pv = reinterpret_cast<float*>(&v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float g = acc[0][n][4 * q + i], u = acc[1][n][4 * q + i];
+          pv[i] = g / (1.0f + expf(-g)) * u;
+        }
+        *reinterpret_cast<float4*>(&G.sa[col][32 * wave + 8 * q + 4 * (lane >> 5)]) = v;
       }
-      *reinterpret_cast<float4*>(&sa[(16 * n + i16) * AS + 16 * wave + 4 * q]) = v;
     }
-  }
   __syncthreads();
-  for (int pass = 0; pass < 2 * kTileN / 8; ++pass) {
+  constexpr int RB = kTileM / 32;   // 32-row blocks per tile
+  for (int pass = 0; pass < RB * kTileN / 8; ++pass) {
     const int bi = pass * 8 + wave * 2 + (lane >> 5);
-    const int j = bi >> 1, blk = bi & 1, jj = lane & 31;
+    const int j = bi / RB, blk = bi % RB, jj = lane & 31;
     float d;
-    const uint32_t w = quant_block32_lanes(sa[j * AS + 32 * blk + jj], a.rot_down, &d);
+    const uint32_t w = quant_block32_lanes(G.sa[j][32 * blk + jj], a.rot_down, &d);
     if (j < T.cnt) {
       const size_t p = (size_t)(T.pbase + j);
       if ((jj & 3) == 0) reinterpret_cast<uint32_t*>(a.hq + p * a.inter + row0 + 32 * blk)[jj >> 2] = w;
@@ -526,58 +620,45 @@ __global__ __launch_bounds__(256) void k_gateup(PrefillArgs a) {
 }
 
 // ------------------------------------------------------------ k_down
-// A workgroup covers 128 rows as two 64-row halves multiplied like the gate and
-// up matrices of k_gateup, so each activation operand read from LDS feeds twice
-// the MFMAs.
+// A workgroup covers 128 rows of one expert's down matrix and one tile of up to
+// 64 pairs (its hq rows), wave w rows 32w..32w+31; the routing weight is applied
+// and each pair's rows are stored in ypair.
 template <int FMT>
-__global__ __launch_bounds__(256) void k_down(PrefillArgs a) {
+__global__ __launch_bounds__(256, 3) void k_down(PrefillArgs a) {
   TileInfo T;
   if (!tile_info(a, T)) return;
-  __shared__ StageLds<FMT, 2> S;
+  __shared__ StageLds<FMT, 1> S;
   __shared__ int s_pair[kTileN];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int row0 = blockIdx.x * 2 * kTileM;
-  const int nn = (T.cnt + 15) >> 4;
+  const int row0 = blockIdx.x * kTileM;
   if (tid < kTileN) s_pair[tid] = a.pairs[T.pbase + min(tid, T.cnt - 1)];
   __syncthreads();
   // hq / dh rows are indexed by the pair's sorted position (padding repeats the last)
   const int8_t* arow = a.hq + (size_t)(T.pbase + min(tid >> 2, T.cnt - 1)) * a.inter;
   const float* adrow = a.dh + (size_t)(T.pbase + min((tid >> 1) & (kTileN - 1), T.cnt - 1)) * a.nb_i;
   const uint8_t* wd = a.down + (size_t)T.e * a.dn_stride;
-  const uint8_t* wd_hi = wd + (size_t)kTileM * a.dn_row_bytes;   // the second 64-row half
-  uint32_t cb[2][4];
+  uint32_t cb[1][4];
   load_codebook<FMT>(a.cb_down + ((size_t)T.e << FMT), cb[0]);
+  float acc[1][2][16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) cb[1][i] = cb[0][i];
-  float acc[2][4][4];
+  for (int n = 0; n < 2; ++n)
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+    for (int r = 0; r < 16; ++r) acc[0][n][r] = 0.0f;
+  stage_loop<FMT, 1>(
+      S, a.nb_i / kKB,
+      [&](StageLoader<FMT, 1>& L, int st) { L.load(wd, wd, a.dn_row_bytes, a.nb_i, row0, st * kKB, arow, adrow); },
+      [&]() { stage_mma<FMT, 1>(S, cb, acc, T.cnt); });
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[m][n][r] = 0.0f;
-  const int nst = a.nb_i / kKB;
-  for (int st = 0; st < nst; ++st) {
-    {
-      StageLoader<FMT, 2> L;
-      L.load(wd, wd_hi, a.dn_row_bytes, a.nb_i, row0, st * kKB, arow, adrow);
-      __syncthreads();
-      L.store(S);
-    }
-    __syncthreads();
-    stage_mma<FMT, 2>(S, cb, acc, nn);
-  }
-  const int i16 = lane & 15, q = lane >> 4;
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int j = 16 * n + i16;
+  for (int n = 0; n < 2; ++n) {
+    const int j = 32 * n + (lane & 31);
     if (j < T.cnt) {
       const int pair = s_pair[j];
       const float g = a.gw[pair];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const float4 v = make_float4(acc[m][n][0] * g, acc[m][n][1] * g, acc[m][n][2] * g, acc[m][n][3] * g);
-        *reinterpret_cast<float4*>(a.ypair + (size_t)pair * a.hidden + row0 + kTileM * m + 16 * wave + 4 * q) = v;
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = make_float4(acc[0][n][4 * q] * g, acc[0][n][4 * q + 1] * g, acc[0][n][4 * q + 2] * g,
+                                     acc[0][n][4 * q + 3] * g);
+        *reinterpret_cast<float4*>(a.ypair + (size_t)pair * a.hidden + row0 + 32 * wave + 8 * q + 4 * (lane >> 5)) = v;
       }
     }
   }
@@ -611,7 +692,7 @@ int launch_gemms(const PrefillArgs& a, int tiles_max, int ntok, float* out, hipS
   int st = launch_check("gateup_mfma");
   if (st) return st;
   {
-    launch_kernel("down_mfma", k_down<FD>, dim3(a.hidden / (2 * kTileM), tiles_max), dim3(256), s, a);
+    launch_kernel("down_mfma", k_down<FD>, dim3(a.hidden / kTileM, tiles_max), dim3(256), s, a);
   }
   if ((st = launch_check("down_mfma"))) return st;
   {
@@ -635,12 +716,10 @@ __global__ __launch_bounds__(256) void k_block_dots_mfma(const uint8_t* __restri
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row0 = blockIdx.x * kTileM, col0 = blockIdx.y * kTileN;
   const int cnt = min(kTileN, ncols - col0);
-  const int nn = (cnt + 15) >> 4;
   const int8_t* arow = xq + (size_t)min(col0 + (tid >> 2), ncols - 1) * ((size_t)nb * 32);
   uint32_t cb[1][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) cb[0][i] = (i < Fmt<FMT>::kCbWords) ? cbw[i] : 0u;
-  const int i16 = lane & 15, q = lane >> 4;
   for (int st = 0; st < nb / kKB; ++st) {
     {
       StageLoader<FMT, 1, false> L;
@@ -650,14 +729,14 @@ __global__ __launch_bounds__(256) void k_block_dots_mfma(const uint8_t* __restri
     }
     __syncthreads();
     stage_int8<FMT, 1>(
-        S, cb, nn, [](int) {},
-        [&](int b, int, int n, const v4i& R) {
-          const int col = col0 + 16 * n + i16;
-          if (16 * n + i16 < cnt) {
+        S, cb, cnt, [](int, int) {},
+        [&](int b, int, int n, const v16i& R) {
+          const int c = 32 * n + (lane & 31);
+          if (c < cnt) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int row = row0 + 16 * wave + 4 * q + r;
-              P[((size_t)col * gridDim.x * kTileM + row) * nb + st * kKB + b] = R[r];
+            for (int r = 0; r < 16; ++r) {
+              const int row = row0 + 32 * wave + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+              P[((size_t)(col0 + c) * gridDim.x * kTileM + row) * nb + st * kKB + b] = R[r];
             }
           }
         });
@@ -712,8 +791,8 @@ extern "C" int qmoe_prefill_layer(const qmoe_layer* L, const float* x, int32_t n
   if (ntok == 0) return QMOE_OK;
   if (!x || !out) QMOE_FAIL(QMOE_E_INVAL, "NULL pointer");
   if (!aligned16(x) || !aligned16(out)) QMOE_FAIL(QMOE_E_INVAL, "x / out not 16-byte aligned");
-  // tile shapes: rows in 64s, K in stages of 8 blocks (guaranteed by the 16-byte row rule)
-  if (L->inter % kTileM || L->hidden % (2 * kTileM) || (L->hidden / 32) % kKB || (L->inter / 32) % kKB)
+  // tile shapes: rows in 128s, K in stages of 8 blocks (256 weights)
+  if (L->inter % kTileM || L->hidden % kTileM || (L->hidden / 32) % kKB || (L->inter / 32) % kKB)
     QMOE_FAIL(QMOE_E_SHAPE, "prefill needs hidden and inter multiples of 256 (hidden=%d inter=%d)", L->hidden,
               L->inter);
   hipStream_t s = as_stream(stream);

@@ -174,7 +174,8 @@ int qmoe_decode_layer_noalloc(const qmoe_layer* L, const float* x, int32_t q, fl
 /* Prefill: ntok tokens through the layer, grouped by expert on the device
  * ([evox3] ladder: layer-major prefill batching). x: fp32 [ntok][hidden];
  * out: fp32 [ntok][hidden]. Deterministic: per token the expert outputs are
- * combined in ascending expert id. */
+ * combined in ascending expert id. hidden and inter must be multiples of 256
+ * (the GEMM tiles: 128 rows, K in stages of 256), else QMOE_E_SHAPE. */
 int qmoe_prefill_layer(const qmoe_layer* L, const float* x, int32_t ntok, float* out,
                        void* ws, size_t ws_bytes, void* stream);
 
@@ -231,10 +232,11 @@ int qmoe_block_dots(int fmt, int64_t rows, int64_t k, const void* w, size_t w_by
 
 /* The same per-block sums for ncols (1..64) int8 columns through the prefill
  * kernels' matrix-core path: the A operand expanded from the packed codes by
- * byte permutes, one int8 MFMA per 32-block and 16-column subtile, as the
- * prefill expert GEMMs compute them ([evox3], table "The optimization ladder":
- * the batched multi-token prefill). xq: int8 [ncols][k]; P: int32
- * [ncols][rows][k/32] (device). rows: a multiple of 64; k: a multiple of 256.
+ * byte permutes, one int8 MFMA (v_mfma_i32_32x32x32_i8) per 32-block and
+ * 32 x 32 tile, as the prefill expert GEMMs compute them ([evox3], table "The
+ * optimization ladder": the batched multi-token prefill). xq: int8
+ * [ncols][k]; P: int32 [ncols][rows][k/32] (device). rows: a multiple of 128;
+ * k: a multiple of 256.
  * Errors as qmoe_matvec (ncols outside 1..64: QMOE_E_SHAPE). */
 int qmoe_block_dots_mfma(int fmt, int64_t rows, int64_t k, const void* w, size_t w_bytes,
                          const int8_t* cb, const int8_t* xq, int32_t ncols, int32_t* P,

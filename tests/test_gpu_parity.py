@@ -77,7 +77,7 @@ def test_block_dots_bit_exact(fmt, rows, k):
     assert np.array_equal(P.cpu().numpy(), P_ref.astype(np.int32))
 
 
-@pytest.mark.parametrize("fmt,rows,k", [(2, 128, 512), (3, 64, 256), (4, 128, 1024), (3, 192, 768)])
+@pytest.mark.parametrize("fmt,rows,k", [(2, 128, 512), (3, 128, 256), (4, 256, 1024), (3, 384, 768)])
 @pytest.mark.parametrize("ncols", [1, 17, 64])
 def test_block_dots_mfma_bit_exact(fmt, rows, k, ncols):
     """The prefill GEMMs' matrix-core path (operand expansion from the packed
