@@ -55,6 +55,7 @@ def parse():
                          "for scaling memory-traffic counters)")
     ap.add_argument("--prefill-only", action="store_true", help="only the 8K-token prefill (for profiling)")
     ap.add_argument("--quantize-only", action="store_true", help="only the weight quantizer (for profiling)")
+    ap.add_argument("--decode-q4-only", action="store_true", help="only the q=4 decode (for profiling)")
     return ap.parse_args()
 
 
@@ -123,6 +124,9 @@ def main():
                           "quantize_fp3": bench_quantize(torch, qm, gen, dev, fmt=3, rows=4096, k=2048)}), flush=True)
         return
     ws = dl.workspace(4)
+    if args.decode_q4_only:
+        print(json.dumps(bench_q4(args, torch, qm, gen, spec, dl, ws, per_expert, dev)[0]), flush=True)
+        return
     toks = torch.from_numpy(gen.tokens(64, spec.hidden, seed=0, stream=7)).to(dev)
     out = torch.empty((4, spec.hidden), dtype=torch.float32, device=dev)
 
@@ -277,10 +281,11 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
+def bench_q4(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
+    """q = 4 decode on groups of four tokens whose top-6 sets overlap (at most 12
+    distinct experts, at least half of them shared by two or more tokens)."""
     res = {}
     K = max(20, args.steps // 2)
-    # ---------------------------------------------------------------- q = 4, forced overlap
     groups, U = [], []
     idx = torch.empty((4, spec.topk), dtype=torch.int32, device=dev)
     gw = torch.empty((4, spec.topk), dtype=torch.float32, device=dev)
@@ -317,6 +322,12 @@ def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
                         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "groups": len(groups), "kernel_us": kern}
     log(f"decode q=4: {ms * 1e3:.2f} us/call, U={np.mean(U):.2f}, {gbs:.1f} GB/s; kernels (us): "
         + ", ".join(f"{k}={v}" for k, v in kern.items()))
+    return res, groups, out
+
+
+def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
+    K = max(20, args.steps // 2)
+    res, groups, out = bench_q4(args, torch, qm, gen, spec, dl, ws, per_expert, dev)
 
     # ablation: the same four columns decoded one call per column (each expert
     # block decoded once per routed column instead of once per group)

@@ -262,23 +262,35 @@ __device__ __forceinline__ void bf16_split3(float v, uint32_t& hi, uint32_t& mid
 // LDS of one stage: NMAT matrices of 128 rows x 8 blocks and 64 columns x 8
 // blocks of activations. Code words and FP3 planes are stored block-major with
 // rows innermost, so the 32 rows an operand read touches are consecutive
-// words. Scales are stored as their bf16 parts: s = (s_hi | s_lo << 16) per
-// (block, row), d = (d_hi | d_mid << 16, d_lo) per (block, column); a lane
-// builds its bf16 MFMA operand (4 bf16, K = 4 (l / 32) + j) with byte permutes:
-// half 0 = (s_hi, s_hi, s_hi, s_lo) x (d_hi, d_mid, d_lo, d_hi), half 1 =
-// (s_lo, s_lo, 0, 0) x (d_mid, d_lo, 0, 0): the six part products.
+// words. (An XOR swizzle of the row index that takes the transposed stores and
+// the two K halves of a read to distinct banks measured no faster.) Scales are
+// stored as their bf16 parts; the bf16 MFMA operands hold 4 bf16 per lane,
+// K = 4 (l / 32) + j.
+//  * Two matrices (kWideD): laid out so that the operands are plain loads: the
+//    weight side is (s_hi, s_lo, s_hi, s_lo) in both halves (one word s_hi |
+//    s_lo << 16, used twice), the activation side (d_hi, d_hi, d_mid, d_mid) in
+//    half 0 and (d_lo, d_lo, 0, 0) in half 1.
+//  * One matrix: the activation side is one (d_hi | d_mid << 16, d_lo) pair
+//    per column, half its size (the down GEMM then fits four workgroups per
+//    compute unit), and a lane builds its operands with byte permutes: half 0 =
+//    (s_hi, s_hi, s_hi, s_lo) x (d_hi, d_mid, d_lo, d_hi), half 1 = (s_lo,
+//    s_lo, 0, 0) x (d_mid, d_lo, 0, 0).
+// Either way the K = 8 sum holds the six part products (s_hi + s_lo)(d_hi +
+// d_mid + d_lo).
 template <int FMT, int NMAT>
 struct StageLds {
+  static constexpr bool kWideD = NMAT == 2;
   static constexpr int LW = Fmt<FMT>::kLoWords;
   static constexpr int XS = kKB * 8 + 4;     // activation words per column (16-byte pieces, spread over banks)
   uint32_t w[NMAT][kKB][LW][kTileM];
   uint32_t h[NMAT][kKB][Fmt<FMT>::kHi ? kTileM : 1];
   uint32_t s[NMAT][kKB][kTileM];           // weight-scale bf16 parts per (block, row)
   uint32_t x[kTileN][XS];
-  u32x2 d[kKB][kTileN];                     // activation-scale bf16 parts per (block, column)
+  // activation-scale words per (block, K half, column), the halves 32 banks apart
+  u32x2 d[kKB][kWideD ? 2 : 1][kWideD ? kTileN + 16 : kTileN];
 };
 
-// The bf16 MFMA operands of K half kh from the stored parts (see StageLds).
+// One-matrix operand builders (see StageLds).
 __device__ __forceinline__ v4s scale_operand_w(uint32_t sp, int kh) {
   const uint32_t w0 = perm(sp, sp, kh ? 0x03020302u : 0x01000100u);   // (s_hi, s_hi) or (s_lo, s_lo)
   return __builtin_bit_cast(v4s, u32x2{w0, kh ? 0u : sp});             // (.., s_hi, s_lo) or (.., 0, 0)
@@ -403,7 +415,12 @@ struct StageLoader {
         for (int k = 0; k < 4; ++k) {
           uint32_t hi, mid, lo;
           bf16_split3(__uint_as_float(v[k]), hi, mid, lo);
-          S.d[4 * cc + k][jj] = u32x2{hi | (mid << 16), lo};
+          if constexpr (StageLds<FMT, NMAT>::kWideD) {
+            S.d[4 * cc + k][0][jj] = u32x2{hi * 0x10001u, mid * 0x10001u};
+            S.d[4 * cc + k][1][jj] = u32x2{lo * 0x10001u, 0u};
+          } else {
+            S.d[4 * cc + k][0][jj] = u32x2{hi | (mid << 16), lo};
+          }
         }
       }
     }
@@ -462,29 +479,42 @@ __device__ __forceinline__ void stage_int8(const StageLds<FMT, NMAT>& S, const u
 // Multiply one stage into fp32 accumulators: acc[m][n][r] (row 32w + 8 (r / 4)
 // + 4 (l / 32) + r % 4, column 32n + l % 32) += float(P) x (weight scale x
 // activation scale), each 32 x 32 tile of scale products formed by the bf16
-// MFMA right where it is consumed (its operands are read once per block).
-template <int FMT, int NMAT>
+// MFMA right where it is consumed (its operands are read once per block). NN:
+// the column subtiles that hold pairs (the caller picks it once per tile, so the
+// accumulators are not copied between two loop forms every stage).
+template <int FMT, int NMAT, int NN>
 __device__ __forceinline__ void stage_mma(const StageLds<FMT, NMAT>& S, const uint32_t cb[NMAT][4],
-                                          float acc[NMAT][2][16], int ncol) {
+                                          float acc[NMAT][2][16]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int kh = lane >> 5;
   const int ra = 32 * wave + (lane & 31);
   v4s sop[NMAT], dop[2];
-  stage_int8<FMT, NMAT>(
-      S, cb, ncol,
-      [&](int b, int nn) {
+  auto hook = [&](int b, int nn) {
+        if constexpr (StageLds<FMT, NMAT>::kWideD) {
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
-          if (n < nn) dop[n] = scale_operand_a(S.d[b][32 * n + (lane & 31)], kh);
+          for (int n = 0; n < 2; ++n)
+            if (n < nn) dop[n] = __builtin_bit_cast(v4s, S.d[b][kh][32 * n + (lane & 31)]);
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) sop[m] = scale_operand_w(S.s[m][b][ra], kh);
-      },
-      [&](int, int m, int n, const v16i& P) {
+          for (int m = 0; m < NMAT; ++m) {
+            const uint32_t sp = S.s[m][b][ra];
+            sop[m] = __builtin_bit_cast(v4s, u32x2{sp, sp});
+          }
+        } else {
+#pragma unroll
+          for (int n = 0; n < 2; ++n)
+            if (n < nn) dop[n] = scale_operand_a(S.d[b][0][32 * n + (lane & 31)], kh);
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) sop[m] = scale_operand_w(S.s[m][b][ra], kh);
+        }
+      };
+  auto use = [&](int, int m, int n, const v16i& P) {
         const v16f pr = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(sop[m], dop[n], v16f{}, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[m][n][r] = fmaf((float)P[r], pr[r], acc[m][n][r]);
-      });
+      };
+  stage_int8_nn<FMT, NMAT, NN>(S, cb, hook, use);
 }
+
 
 struct PrefillArgs {
   const uint8_t* gate;
@@ -544,6 +574,16 @@ __device__ __forceinline__ void stage_loop(StageLds<FMT, NMAT>& S, int nst, Load
   }
 }
 
+// The stage loop of one tile with the subtile count fixed for the whole loop.
+template <int FMT, int NMAT, typename Load>
+__device__ __forceinline__ void tile_mma(StageLds<FMT, NMAT>& S, const uint32_t cb[NMAT][4], float acc[NMAT][2][16],
+                                         int ncol, int nst, Load&& load) {
+  if (ncol > 32)
+    stage_loop<FMT, NMAT>(S, nst, load, [&]() { stage_mma<FMT, NMAT, 2>(S, cb, acc); });
+  else
+    stage_loop<FMT, NMAT>(S, nst, load, [&]() { stage_mma<FMT, NMAT, 1>(S, cb, acc); });
+}
+
 // ------------------------------------------------------------ k_gateup
 // A workgroup multiplies 128 rows of gate and of up with one tile of up to 64
 // pairs; wave w owns rows 32w..32w+31 of both matrices and all the tile's
@@ -558,7 +598,7 @@ struct GateupLds {
 };
 
 template <int FMT>
-__global__ __launch_bounds__(256, FMT == 4 ? 2 : 3) void k_gateup(PrefillArgs a) {
+__global__ __launch_bounds__(256, FMT == 2 ? 3 : 2) void k_gateup(PrefillArgs a) {
   TileInfo T;
   if (!tile_info(a, T)) return;
   __shared__ GateupLds<FMT> G;
@@ -582,10 +622,9 @@ __global__ __launch_bounds__(256, FMT == 4 ? 2 : 3) void k_gateup(PrefillArgs a)
     for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.0f;
-  stage_loop<FMT, 2>(
-      S, a.nb_h / kKB,
-      [&](StageLoader<FMT, 2>& L, int st) { L.load(wg, wu, a.gu_row_bytes, a.nb_h, row0, st * kKB, arow, adrow); },
-      [&]() { stage_mma<FMT, 2>(S, cb, acc, T.cnt); });
+  tile_mma<FMT, 2>(S, cb, acc, T.cnt, a.nb_h / kKB, [&](StageLoader<FMT, 2>& L, int st) {
+    L.load(wg, wu, a.gu_row_bytes, a.nb_h, row0, st * kKB, arow, adrow);
+  });
   // SwiGLU into LDS as [pair][row], then requantize each (pair, 32-row block)
   __syncthreads();
 #pragma unroll
@@ -624,7 +663,7 @@ __global__ __launch_bounds__(256, FMT == 4 ? 2 : 3) void k_gateup(PrefillArgs a)
 // 64 pairs (its hq rows), wave w rows 32w..32w+31; the routing weight is applied
 // and each pair's rows are stored in ypair.
 template <int FMT>
-__global__ __launch_bounds__(256, 3) void k_down(PrefillArgs a) {
+__global__ __launch_bounds__(256, FMT == 4 ? 3 : 4) void k_down(PrefillArgs a) {
   TileInfo T;
   if (!tile_info(a, T)) return;
   __shared__ StageLds<FMT, 1> S;
@@ -644,10 +683,9 @@ __global__ __launch_bounds__(256, 3) void k_down(PrefillArgs a) {
   for (int n = 0; n < 2; ++n)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[0][n][r] = 0.0f;
-  stage_loop<FMT, 1>(
-      S, a.nb_i / kKB,
-      [&](StageLoader<FMT, 1>& L, int st) { L.load(wd, wd, a.dn_row_bytes, a.nb_i, row0, st * kKB, arow, adrow); },
-      [&]() { stage_mma<FMT, 1>(S, cb, acc, T.cnt); });
+  tile_mma<FMT, 1>(S, cb, acc, T.cnt, a.nb_i / kKB, [&](StageLoader<FMT, 1>& L, int st) {
+    L.load(wd, wd, a.dn_row_bytes, a.nb_i, row0, st * kKB, arow, adrow);
+  });
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const int j = 32 * n + (lane & 31);
