@@ -67,19 +67,26 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ W, 
 }
 
 // ------------------------------------------------------------ router, many tokens
-// A workgroup computes a 32-expert x 32-token tile of logits; each thread owns
-// 2 experts x 2 tokens and evaluates each logit on its own, in the same fixed
-// order as the wave router: per 32-block a sequential fp64 sum of the exact
-// fp16 x fp32 products, then the stride-halving tree over the (zero-padded)
-// power-of-two block count. The tree is evaluated depth first: its leaves are
-// visited in bit-reversed order and partial sums are kept per level like the
-// digits of a binary counter (level k holds a sum of 2^k leaves). Operands are
-// staged in LDS as fp32, 4 leaves at a time (the fp16 weights widened exactly
-// once per workgroup), and widened to fp64 in registers at each use: exact, so
-// the products are those of an all-fp64 evaluation, at half the LDS bytes.
+// A workgroup computes a 32-expert x 32-token tile of logits on the fp64 matrix
+// cores, each logit in the same fixed order as the wave router: per 32-block a
+// sequential fp64 sum of the exact fp16 x fp32 products, then the stride-halving
+// tree over the (zero-padded) power-of-two block count. Wave w owns the 16 x 16
+// subtile of experts 16 (w & 1).. and tokens 16 (w >> 1)... One
+// v_mfma_f64_16x16x4f64 adds its four products to the accumulator one after the
+// other in K order, each step rounded as a fused multiply-add (checked on the
+// GPU against the sequential chain on special and random operands), and operand
+// lane l holds row (or column) l % 16 at K = l / 16; so a block is 8
+// instructions, step s taking K = 4s + l / 16, from +0. Result register r of
+// lane l is expert 4r + l / 16, token l % 16 of the subtile. The tree is
+// evaluated depth first: its leaves are visited in bit-reversed order and
+// partial sums are kept per level like the digits of a binary counter (level k
+// holds a sum of 2^k leaves). Operands are staged in LDS as fp32, 4 leaves at a
+// time (the fp16 weights widened exactly once per workgroup), and widened to
+// fp64 at each use: exact, so the products are those of an all-fp64 evaluation.
+typedef double v4d __attribute__((ext_vector_type(4)));
 constexpr int kRtE = 32, kRtT = 32, kRtLeaves = 4;
-constexpr int kRtStride = kRtLeaves * 32 + 4;   // floats per LDS row (+4: 16-byte reads of 16 rows hit distinct banks)
-constexpr int kRtLevels = 9;                    // up to 256 blocks (hidden <= 8192)
+constexpr int kRtStride = 36;   // floats per LDS row: a read's 16 rows x 4 K lanes fall in distinct banks
+constexpr int kRtLevels = 9;    // up to 256 blocks (hidden <= 8192)
 
 __device__ __forceinline__ int bit_reverse(int v, int bits) {
   return (int)(__builtin_bitreverse32((uint32_t)v) >> (32 - bits));
@@ -88,11 +95,12 @@ __device__ __forceinline__ int bit_reverse(int v, int bits) {
 __global__ __launch_bounds__(256) void k_router_tiles(const uint16_t* __restrict__ W, const float* __restrict__ x,
                                                       int ntok, int E, int H, const double* __restrict__ bias,
                                                       double* __restrict__ logits) {
-  __shared__ float s_w[kRtE][kRtStride];
-  __shared__ float s_x[kRtT][kRtStride];
-  const int tid = threadIdx.x;
+  __shared__ float s_w[kRtLeaves][kRtE][kRtStride];
+  __shared__ float s_x[kRtLeaves][kRtT][kRtStride];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int e_base = blockIdx.x * kRtE, t_base = blockIdx.y * kRtT;
-  const int ei = tid >> 4, ti = tid & 15;   // experts ei, ei+16; tokens ti, ti+16
+  const int we = 16 * (wave & 1), wt = 16 * (wave >> 1);   // the wave's subtile
+  const int row = lane & 15, kg = lane >> 4;                // operand row / column, K lane group
   const int nb = H >> 5;
   int L = 0;
   while ((1 << L) < nb) ++L;
@@ -129,34 +137,21 @@ __global__ __launch_bounds__(256) void k_router_tiles(const uint16_t* __restrict
       __syncthreads();   // the previous chunk's reads are done
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        *reinterpret_cast<float4*>(&s_w[lr][lk * 32 + 16 * lh + 4 * j]) =
+        *reinterpret_cast<float4*>(&s_w[lk][lr][16 * lh + 4 * j]) =
             make_float4(wv[4 * j], wv[4 * j + 1], wv[4 * j + 2], wv[4 * j + 3]);
-        *reinterpret_cast<float4*>(&s_x[lr][lk * 32 + 16 * lh + 4 * j]) = xv[j];
+        *reinterpret_cast<float4*>(&s_x[lk][lr][16 * lh + 4 * j]) = xv[j];
       }
       __syncthreads();
     }
 #pragma unroll 1
     for (int k = 0; k < kRtLeaves; ++k) {
       const int i = i0 + k;   // depth-first leaf index (uniform)
-      double acc[4] = {0.0, 0.0, 0.0, 0.0};
-      const bool real = bit_reverse(i, L) < nb;   // padding leaves are +0
-      if (real) {
-#pragma unroll 2
-        for (int j = 0; j < 32; j += 4) {
-          const float4 w0 = *reinterpret_cast<const float4*>(&s_w[ei][k * 32 + j]);
-          const float4 w1 = *reinterpret_cast<const float4*>(&s_w[ei + 16][k * 32 + j]);
-          const float4 x0 = *reinterpret_cast<const float4*>(&s_x[ti][k * 32 + j]);
-          const float4 x1 = *reinterpret_cast<const float4*>(&s_x[ti + 16][k * 32 + j]);
-          const float fw0[4] = {w0.x, w0.y, w0.z, w0.w}, fw1[4] = {w1.x, w1.y, w1.z, w1.w};
-          const float fx0[4] = {x0.x, x0.y, x0.z, x0.w}, fx1[4] = {x1.x, x1.y, x1.z, x1.w};
+      v4d acc = {0.0, 0.0, 0.0, 0.0};
+      if (bit_reverse(i, L) < nb) {   // padding leaves are +0
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const double a0 = fw0[u], a1 = fw1[u], b0 = fx0[u], b1 = fx1[u];
-            acc[0] = fma(a0, b0, acc[0]);
-            acc[1] = fma(a0, b1, acc[1]);
-            acc[2] = fma(a1, b0, acc[2]);
-            acc[3] = fma(a1, b1, acc[3]);
-          }
+        for (int st = 0; st < 8; ++st) {
+          const double a = s_w[k][we + row][4 * st + kg], bx = s_x[k][wt + row][4 * st + kg];
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bx, acc, 0, 0, 0);
         }
       }
       // push the leaf: carry through the occupied levels (bits of i), left + right
@@ -181,7 +176,7 @@ __global__ __launch_bounds__(256) void k_router_tiles(const uint16_t* __restrict
   // after P2 = 2^L leaves the whole tree sits at level L
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int e = e_base + ei + 16 * (c >> 1), t = t_base + ti + 16 * (c & 1);
+    const int e = e_base + we + 4 * c + kg, t = t_base + wt + row;
     double v = lvl[c][0];
 #pragma unroll
     for (int lv = 1; lv < kRtLevels; ++lv)
