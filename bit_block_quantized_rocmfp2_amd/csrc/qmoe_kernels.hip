@@ -73,8 +73,9 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ W, 
 // tree over the (zero-padded) power-of-two block count. Wave w owns the 16 x 16
 // subtile of experts 16 (w & 1).. and tokens 16 (w >> 1)... One
 // v_mfma_f64_16x16x4f64 adds its four products to the accumulator one after the
-// other in K order, each step rounded as a fused multiply-add (checked on the
-// GPU against the sequential chain on special and random operands), and operand
+// other in K order, each step rounded as a fused multiply-add (measured on the
+// GPU on operands whose sum depends on the order; the tiled-logits parity tests
+// hold every logit to the oracle's sequential order bit for bit), and operand
 // lane l holds row (or column) l % 16 at K = l / 16; so a block is 8
 // instructions, step s taking K = 4s + l / 16, from +0. Result register r of
 // lane l is expert 4r + l / 16, token l % 16 of the subtile. The tree is
