@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--prefill-only", action="store_true", help="only the 8K-token prefill (for profiling)")
     ap.add_argument("--quantize-only", action="store_true", help="only the weight quantizer (for profiling)")
     ap.add_argument("--decode-q4-only", action="store_true", help="only the q=4 decode (for profiling)")
+    ap.add_argument("--prefill-small-sweep", action="store_true",
+                    help="only: prefill time against the small-expert threshold over batch sizes")
     return ap.parse_args()
 
 
@@ -118,6 +120,9 @@ def main():
     if args.prefill_only:
         res = bench_prefill(torch, qm, gen, spec, dl, dev)
         print(json.dumps({"prefill_8k": res}), flush=True)
+        return
+    if args.prefill_small_sweep:
+        print(json.dumps({"prefill_small_sweep": bench_prefill_small_sweep(torch, qm, gen, spec, dl, dev)}), flush=True)
         return
     if args.quantize_only:
         print(json.dumps({"quantize_fp2": bench_quantize(torch, qm, gen, dev),
@@ -664,19 +669,68 @@ def bench_prefill(torch, qm, gen, spec, dl, dev):
     torch.cuda.synchronize()
     kern = {}
     for name in ("quant_act", "router", "topk", "group_count", "group_scan", "group_scatter", "gateup_mfma",
-                 "down_mfma", "combine"):
+                 "down_mfma", "gateup_small", "down_small", "combine"):
         avg, _ = kernel_avg_ms(qm, name)
         if avg:
             kern[name] = round(avg * 1e3, 1)
     qm.qmoe_timing_enable(False)
-    gemm_ms = (kern.get("gateup_mfma", 0) + kern.get("down_mfma", 0)) / 1e3
+    # the expert products of both branches: MFMA tiles and the matvec path of the
+    # experts with at most four pairs
+    gemm_ms = sum(kern.get(k, 0) for k in ("gateup_mfma", "down_mfma", "gateup_small", "down_small")) / 1e3
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None
+    lay = qm.qmoe_workspace_layout(desc, T)
+    E = spec.n_experts
+    counts = ws[lay["group"]: lay["group"] + 4 * E].cpu().numpy().view(np.int32)
+    th = qm.PREFILL_SMALL_DEFAULT
+    small = (counts >= 1) & (counts <= th)
+    branches = {"small_threshold": th, "mfma_experts": int(np.count_nonzero(counts > th)),
+                "mfma_pairs": int(counts[counts > th].sum()), "small_experts": int(np.count_nonzero(small)),
+                "small_pairs": int(counts[small].sum()), "mfma_tiles_of_64": int(np.sum((counts[counts > th] + 63) // 64))}
     log(f"prefill 8K: {ms:.3f} ms, {T / (ms * 1e-3):.0f} tok/s, {tops:.1f} TOPS; kernels (us): "
         + ", ".join(f"{k}={v}" for k, v in kern.items()))
     return {"ms_per_call": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1), "int8_TOPS": round(tops, 2),
             "frac_int8_mfma_peak": round(tops / INT8_MFMA_PEAK_TOPS, 4), "kernel_us": kern,
-            "gemm_int8_TOPS": round(gemm_tops, 2) if gemm_tops else None,
+            "gemm_int8_TOPS": round(gemm_tops, 2) if gemm_tops else None, "branches": branches,
             "gemm_frac_int8_mfma_peak": round(gemm_tops / INT8_MFMA_PEAK_TOPS, 4) if gemm_tops else None}
+
+
+def bench_prefill_small_sweep(torch, qm, gen, spec, dl, dev):
+    """Prefill time against qmoe_prefill_layer_ex's small-expert threshold (0 = all
+    experts on MFMA tiles) for 32 .. 8192 tokens, with and without the Zipf(1.1)
+    router bias. The thresholds are timed in rounds that alternate their order
+    (medians of 6 rounds), since the first timing after a change of input runs
+    slow."""
+    bias = torch.from_numpy(gen.zipf_bias(spec.n_experts)).to(dev)
+    rows = []
+    for zipf in (True, False):
+        desc = qm.make_layer(spec.hidden, spec.inter, spec.n_experts, spec.topk, spec.fmt_gate, spec.fmt_up,
+                             spec.fmt_down, spec.rot_gateup, spec.rot_down, dl.w_router, bias if zipf else None,
+                             dl.gate, dl.up, dl.down, dl.cb_gate, dl.cb_up, dl.cb_down)
+        for T in (32, 128, 512, 2048, 8192):
+            x = torch.from_numpy(gen.tokens(T, spec.hidden, seed=0, stream=9)).to(dev)
+            out = torch.empty_like(x)
+            ws = torch.zeros(qm.qmoe_workspace_bytes(desc, T), dtype=torch.uint8, device=dev)
+            thresholds = (0, 1, 2, 4)
+            samples = {sp: [] for sp in thresholds}
+            for _ in range(3):
+                qm.qmoe_prefill_layer_ex(desc, x, out, ws, 0)
+            for rnd in range(6):
+                for sp in (thresholds if rnd % 2 == 0 else thresholds[::-1]):
+                    reps = 10 if T <= 2048 else 3
+                    qm.qmoe_prefill_layer_ex(desc, x, out, ws, sp)
+                    with Timer(torch) as t:
+                        for _ in range(reps):
+                            qm.qmoe_prefill_layer_ex(desc, x, out, ws, sp)
+                    samples[sp].append(t.ms / reps * 1e3)
+            lay = qm.qmoe_workspace_layout(desc, T)
+            counts = ws[lay["group"]: lay["group"] + 4 * spec.n_experts].cpu().numpy().view(np.int32)
+            row = {"zipf": zipf, "tokens": T, "us_median_by_threshold": {sp: round(float(np.median(v)), 1)
+                                                                         for sp, v in samples.items()},
+                   "experts_1_to_4_pairs": int(((counts >= 1) & (counts <= 4)).sum()),
+                   "experts_over_4_pairs": int((counts > 4).sum())}
+            log(f"prefill small-expert sweep: {row}")
+            rows.append(row)
+    return rows
 
 
 def oracle_threads():

@@ -77,6 +77,8 @@ def _load():
         "qmoe_decode_layer_noalloc": (c_int, [POINTER(qmoe_layer), c_void_p, c_int32, c_void_p, c_void_p]),
         "qmoe_prefill_layer": (c_int, [POINTER(qmoe_layer), c_void_p, c_int32, c_void_p, c_void_p, c_size_t,
                                        c_void_p]),
+        "qmoe_prefill_layer_ex": (c_int, [POINTER(qmoe_layer), c_void_p, c_int32, c_void_p, c_void_p, c_size_t,
+                                          c_int32, c_void_p]),
         "qmoe_matvec_workspace_bytes": (c_size_t, [c_int64, c_int32]),
         "qmoe_matvec": (c_int, [c_int, c_int64, c_int64, c_void_p, c_size_t, c_void_p, c_int32, c_void_p, c_int32,
                                 c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -109,7 +111,8 @@ LIB = _load()
 EXPORTED = (
     "qmoe_strerror", "qmoe_last_error", "qmoe_version", "qmoe_block_bytes", "qmoe_packed_bytes", "qmoe_pack",
     "qmoe_unpack", "qmoe_layer_check", "qmoe_workspace_bytes", "qmoe_workspace_layout", "qmoe_route",
-    "qmoe_decode_layer", "qmoe_decode_noalloc_max_bytes", "qmoe_decode_layer_noalloc", "qmoe_prefill_layer", "qmoe_matvec_workspace_bytes", "qmoe_matvec", "qmoe_quant_act",
+    "qmoe_decode_layer", "qmoe_decode_noalloc_max_bytes", "qmoe_decode_layer_noalloc", "qmoe_prefill_layer", "qmoe_prefill_layer_ex",
+    "qmoe_matvec_workspace_bytes", "qmoe_matvec", "qmoe_quant_act",
     "qmoe_block_dots", "qmoe_block_dots_mfma", "qmoe_matvec_expanded_workspace_bytes", "qmoe_matvec_expanded",
     "qmoe_quantize_workspace_bytes", "qmoe_quantize", "qmoe_timing_enable", "qmoe_timing_read", "qmoe_probe_read",
     "qmoe_probe_mfma", "qmoe_probe_valu",
@@ -232,6 +235,15 @@ def qmoe_decode_layer_noalloc(L, x, out, stream=None) -> None:
 def qmoe_prefill_layer(L, x, out, ws, stream=None) -> None:
     _check(LIB.qmoe_prefill_layer(ctypes.byref(L), _ptr(x), x.shape[0], _ptr(out), _ptr(ws), _nbytes(ws),
                                   _stream(stream)), "qmoe_prefill_layer")
+
+
+# QMOE_PREFILL_SMALL_DEFAULT of qmoe.h: the small-expert threshold of qmoe_prefill_layer
+PREFILL_SMALL_DEFAULT = 2
+
+
+def qmoe_prefill_layer_ex(L, x, out, ws, small_pairs, stream=None) -> None:
+    _check(LIB.qmoe_prefill_layer_ex(ctypes.byref(L), _ptr(x), x.shape[0], _ptr(out), _ptr(ws), _nbytes(ws),
+                                     small_pairs, _stream(stream)), "qmoe_prefill_layer_ex")
 
 
 def qmoe_matvec(fmt, rows, k, w, cb, rot, x, y, ws, stream=None) -> None:

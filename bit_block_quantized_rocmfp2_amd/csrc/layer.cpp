@@ -99,8 +99,9 @@ extern "C" int qmoe_workspace_layout(const qmoe_layer* L, int32_t max_tokens, qm
   o->plan = take(4096);
   o->hq = take(slots * I);
   o->dh = take(slots * (I / 32) * 4);
-  // counts[E], offsets[E+1], cursor[E], pairs[T*K], tile list (2 int32 per tile)
-  o->group = take(4 * (3 * E + 1) + 4 * T * K + 8 * (T * K + E) + 4096);
+  // counts[E], offsets[E+1], cursor[E], pairs[T*K], tile list (2 int32 per tile),
+  // small-expert count and list[E]
+  o->group = take(4 * (3 * E + 1) + 4 * T * K + 8 * (T * K + E) + 4 * (E + 1) + 4096);
   o->ypair = take(T * K * H * 4);
   o->total = off;
   return QMOE_OK;

@@ -389,11 +389,12 @@ __device__ __forceinline__ void gateup_epilogue(const DecodeArgs& a, uint32_t ma
 }
 
 // The gate and up rows row0 .. row0+RPW-1 of expert e against the routed
-// columns: per-lane partial sums over the lane's blocks (NBL consecutive
-// blocks per lane and pass).
+// columns (column t: quantized row xcol[t], scales dcol[t]): per-lane partial
+// sums over the lane's blocks (NBL consecutive blocks per lane and pass).
 template <int FMT, int Q, int RPW>
-__device__ __forceinline__ void gateup_stream(const DecodeArgs& a, int e, uint32_t mask, int row0, float (&ag)[RPW][Q],
-                                              float (&au)[RPW][Q]) {
+__device__ __forceinline__ void gateup_stream(const DecodeArgs& a, int e, uint32_t mask, int row0,
+                                              const int8_t* const (&xcol)[Q], const float* const (&dcol)[Q],
+                                              float (&ag)[RPW][Q], float (&au)[RPW][Q]) {
   constexpr int NBL = (FMT == 4) ? 1 : 2;
   const int lane = threadIdx.x & 63;
   const uint8_t* gbase = a.gate + (size_t)e * a.gu_stride;
@@ -414,7 +415,7 @@ __device__ __forceinline__ void gateup_stream(const DecodeArgs& a, int e, uint32
       Acts<NBL> act[Q];
 #pragma unroll
       for (int t = 0; t < Q; ++t)
-        if (mask >> t & 1) act[t].load(a.xq + (size_t)t * nb * 32, a.dx + (size_t)t * nb, b);
+        if (mask >> t & 1) act[t].load(xcol[t], dcol[t], b);
       Blocks<FMT, NBL> bg[RPW], bu[RPW];
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
@@ -451,7 +452,14 @@ __device__ __forceinline__ void gateup_item(const DecodeArgs& a, int e, uint32_t
   constexpr int RPW = 4;
   const int wave = threadIdx.x >> 6;
   float ag[RPW][Q], au[RPW][Q];
-  gateup_stream<FMT, Q, RPW>(a, e, mask, rb * 32 + wave * RPW, ag, au);
+  const int8_t* xcol[Q];
+  const float* dcol[Q];
+#pragma unroll
+  for (int t = 0; t < Q; ++t) {   // the decode tokens' rows are consecutive
+    xcol[t] = a.xq + (size_t)t * a.nb_h * 32;
+    dcol[t] = a.dx + (size_t)t * a.nb_h;
+  }
+  gateup_stream<FMT, Q, RPW>(a, e, mask, rb * 32 + wave * RPW, xcol, dcol, ag, au);
   gateup_epilogue<Q, RPW>(a, mask, u, rb, ag, au, s_a);
 }
 
@@ -933,7 +941,174 @@ int launch_decode_q(const DecodeArgs& a, int U_max, int fg, int fd, hipStream_t 
   return launch_decode_t<4, 4, Q>(a, U_max, s);
 }
 
+// ------------------------------------------------------------ prefill: experts with few pairs
+// Experts that 1 .. kPrefillSmallPairs pairs of a prefill batch route to would
+// fill an MFMA tile with padding; their pairs take the q <= 4 matvec arithmetic
+// instead: each weight block is loaded and expanded once and dotted (sdot4)
+// with every pair of the expert. Workgroup (x, y) serves listed expert y (those
+// beyond the device-side count return at once); its pairs are the columns.
+struct SmallArgs {
+  DecodeArgs d;   // weights, codebooks, shapes, rot_down, dn_lpr_log2
+  PrefillSmall p;
+};
+
+// 32 rows of gate and up per pass (8 waves x 4 rows, as gateup_item),
+// kSmallGateupPasses passes per workgroup.
+constexpr int kSmallGateupPasses = 2;
+template <int FMT>
+__global__ __launch_bounds__(512) void k_pf_gateup_small(SmallArgs sa) {
+  constexpr int Q = kPrefillSmallPairs, RPW = 4;
+  if ((int)blockIdx.y >= *sa.p.nsmall) return;
+  const DecodeArgs& a = sa.d;
+  const int e = sa.p.small[blockIdx.y];
+  const int cnt = sa.p.counts[e], pbase = sa.p.offsets[e];
+  const uint32_t mask = (1u << cnt) - 1u;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ float s_a[4][32];
+  const int8_t* xcol[Q];
+  const float* dcol[Q];
+#pragma unroll
+  for (int t = 0; t < Q; ++t) {   // unused columns repeat the last pair's row (masked out)
+    const int tok = sa.p.pairs[pbase + min(t, cnt - 1)] / a.K;
+    xcol[t] = sa.p.xq + (size_t)tok * a.nb_h * 32;
+    dcol[t] = sa.p.dx + (size_t)tok * a.nb_h;
+  }
+  for (int pass = 0; pass < kSmallGateupPasses; ++pass) {
+    const int rb = blockIdx.x * kSmallGateupPasses + pass;
+    if (rb * 32 >= a.inter) break;   // uniform
+    float ag[RPW][Q], au[RPW][Q];
+    gateup_stream<FMT, Q, RPW>(a, e, mask, rb * 32 + wave * RPW, xcol, dcol, ag, au);
+    gateup_wave_swiglu<Q, RPW>(mask, ag, au, s_a, wave * RPW);
+    __syncthreads();
+    // requantize the 32-row block of each pair: half-wave h of wave w takes column 2w + h
+    if (wave < Q / 2) {
+      const int t = 2 * wave + (lane >> 5), j = lane & 31;
+      const bool act = t < cnt;
+      float d;
+      const uint32_t w = quant_block32_lanes(act ? s_a[t][j] : 0.0f, a.rot_down, &d);
+      if (act) {
+        const size_t pos = (size_t)(pbase + t);
+        if ((j & 3) == 0) reinterpret_cast<uint32_t*>(sa.p.hq + pos * a.inter + (size_t)rb * 32)[j >> 2] = w;
+        if (j == 0) sa.p.dh[pos * a.nb_i + rb] = d;
+      }
+    }
+    __syncthreads();   // s_a is rewritten by the next pass
+  }
+}
+
+// Down rows as k_down (lanes per row 2^dn_lpr_log2, NBL blocks per lane and
+// pass), kSmallDownPasses row groups per workgroup; each block expanded once for
+// all the expert's pairs.
+constexpr int kSmallDownPasses = 8;
+template <int FMT>
+__global__ __launch_bounds__(256) void k_pf_down_small(SmallArgs sa) {
+  constexpr int Q = kPrefillSmallPairs;
+  constexpr int NBL = (FMT == 4) ? 1 : 2;
+  if ((int)blockIdx.y >= *sa.p.nsmall) return;
+  const DecodeArgs& a = sa.d;
+  const int e = sa.p.small[blockIdx.y];
+  const int cnt = sa.p.counts[e], pbase = sa.p.offsets[e];
+  const int lpr_log2 = a.dn_lpr_log2, lpr = 1 << lpr_log2;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sub = lane >> lpr_log2, sl = lane & (lpr - 1);
+  const int nb = a.nb_i;
+  uint32_t cb[4];
+  load_codebook<FMT>(a.cb_down + ((size_t)e << FMT), cb);
+  for (int pass = 0; pass < kSmallDownPasses; ++pass) {
+    const int row = ((blockIdx.x * kSmallDownPasses + pass) * 4 + wave) * (64 >> lpr_log2) + sub;
+    const bool row_ok = row < a.hidden;
+    const uint8_t* wrow = a.down + (size_t)e * a.dn_stride + (size_t)min(row, a.hidden - 1) * a.dn_row_bytes;
+    float acc[Q];
+#pragma unroll
+    for (int t = 0; t < Q; ++t) acc[t] = 0.0f;
+    for (int c0 = 0; c0 < nb; c0 += lpr * NBL) {
+      const int b = c0 + sl * NBL;
+      if (row_ok && b < nb) {
+        Blocks<FMT, NBL> bl;
+        bl.load(wrow, nb, b);
+        Acts<NBL> act[Q];
+#pragma unroll
+        for (int t = 0; t < Q; ++t)
+          if (t < cnt) act[t].load(sa.p.hq + (size_t)(pbase + t) * a.inter, sa.p.dh + (size_t)(pbase + t) * nb, b);
+#pragma unroll
+        for (int i = 0; i < NBL; ++i) {
+          uint32_t w[8];
+          bl.expand(i, cb, w);
+          const float sw = bl.scale(i);
+#pragma unroll
+          for (int t = 0; t < Q; ++t)
+            if (t < cnt) acc[t] = fmaf((float)block_dot(w, act[t].q[i]), sw * act[t].d[i], acc[t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < Q; ++t) {
+      const float v = group_sum(acc[t], lpr);
+      if (t < cnt && sl == 0 && row_ok) {
+        const int pair = sa.p.pairs[pbase + t];
+        sa.p.ypair[(size_t)pair * a.hidden + row] = v * sa.p.gw[pair];
+      }
+    }
+  }
+}
+
+template <int FG, int FD>
+int launch_small_t(const SmallArgs& sa, hipStream_t s) {
+  const DecodeArgs& a = sa.d;
+  const int rb = a.inter / 32;
+  launch_kernel("gateup_small", k_pf_gateup_small<FG>,
+                dim3((rb + kSmallGateupPasses - 1) / kSmallGateupPasses, a.E), dim3(512), s, sa);
+  int st = launch_check("gateup_small");
+  if (st) return st;
+  const int rows_per_wg = 4 * (64 >> a.dn_lpr_log2) * kSmallDownPasses;
+  launch_kernel("down_small", k_pf_down_small<FD>, dim3((a.hidden + rows_per_wg - 1) / rows_per_wg, a.E), dim3(256),
+                s, sa);
+  return launch_check("down_small");
+}
+
 }  // namespace
+
+namespace qmoe {
+
+int launch_prefill_small(const PrefillSmall& p, hipStream_t s) {
+  const qmoe_layer* L = p.L;
+  FormatInfo fg, fd;
+  format_info(L->fmt_gate, &fg);
+  format_info(L->fmt_down, &fd);
+  SmallArgs sa{};
+  DecodeArgs& a = sa.d;
+  a.gate = static_cast<const uint8_t*>(L->gate);
+  a.up = static_cast<const uint8_t*>(L->up);
+  a.down = static_cast<const uint8_t*>(L->down);
+  a.cb_gate = L->cb_gate;
+  a.cb_up = L->cb_up;
+  a.cb_down = L->cb_down;
+  a.hidden = L->hidden;
+  a.inter = L->inter;
+  a.E = L->n_experts;
+  a.K = L->topk;
+  a.rot_down = L->rot_down;
+  a.nb_h = L->hidden / 32;
+  a.nb_i = L->inter / 32;
+  a.gu_row_bytes = (size_t)a.nb_h * fg.block_bytes;
+  a.gu_stride = a.gu_row_bytes * L->inter;
+  a.dn_row_bytes = (size_t)a.nb_i * fd.block_bytes;
+  a.dn_stride = a.dn_row_bytes * L->hidden;
+  a.dn_lpr_log2 = ilog2(lanes_per_row(a.nb_i, L->fmt_down == QMOE_FP4 ? 1 : 2));
+  sa.p = p;
+  const int g = L->fmt_gate, d = L->fmt_down;
+  if (g == 2 && d == 3) return launch_small_t<2, 3>(sa, s);
+  if (g == 2 && d == 2) return launch_small_t<2, 2>(sa, s);
+  if (g == 2 && d == 4) return launch_small_t<2, 4>(sa, s);
+  if (g == 3 && d == 3) return launch_small_t<3, 3>(sa, s);
+  if (g == 3 && d == 2) return launch_small_t<3, 2>(sa, s);
+  if (g == 3 && d == 4) return launch_small_t<3, 4>(sa, s);
+  if (g == 4 && d == 3) return launch_small_t<4, 3>(sa, s);
+  if (g == 4 && d == 2) return launch_small_t<4, 2>(sa, s);
+  return launch_small_t<4, 4>(sa, s);
+}
+
+}  // namespace qmoe
 
 extern "C" int qmoe_decode_layer(const qmoe_layer* L, const float* x, int32_t q, float* out, void* ws,
                                  size_t ws_bytes, void* stream) {

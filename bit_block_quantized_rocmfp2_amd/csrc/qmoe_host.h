@@ -76,6 +76,29 @@ int device_cu_count();
 // alignment, size); fills *fi.
 int check_matrix(int fmt, int64_t rows, int64_t k, const void* w, size_t w_bytes, const int8_t* cb, FormatInfo* fi);
 
+// Prefill experts routed by 1 .. small_pairs pairs (at most kPrefillSmallPairs;
+// the grouping lists them: nsmall[0] experts in small[]) go through the decode
+// path's matvec arithmetic instead of a mostly empty MFMA tile
+// (qmoe_decode.hip): gate/up, SwiGLU and requantization into the hq / dh rows
+// of their sorted pair positions, then down into the ypair rows of their pair
+// indices, times the pair's routing weight.
+constexpr int kPrefillSmallPairs = 4;
+struct PrefillSmall {
+  const qmoe_layer* L;
+  const int8_t* xq;        // every token's quantized activations [ntok][hidden]
+  const float* dx;         // and their block scales [ntok][hidden / 32]
+  const int32_t* counts;   // pairs per expert
+  const int32_t* offsets;  // first sorted position per expert
+  const int32_t* pairs;    // pair indices t * K + s by sorted position
+  const int32_t* nsmall;   // number of listed experts (device)
+  const int32_t* small;    // their ids, ascending
+  const float* gw;         // routing weight per pair index
+  int8_t* hq;              // [npairs][inter] by sorted position
+  float* dh;               // [npairs][inter / 32]
+  float* ypair;            // [npairs][hidden] by pair index
+};
+int launch_prefill_small(const PrefillSmall& p, hipStream_t s);
+
 // Launch helpers shared by the entry points (qmoe_kernels.hip).
 int launch_quant(const float* x, int64_t nblocks, int rot, int8_t* xq, float* dx, hipStream_t s);
 int launch_route(const qmoe_layer* L, const float* x, int32_t ntok, double* logits, int32_t* idx, float* gw,

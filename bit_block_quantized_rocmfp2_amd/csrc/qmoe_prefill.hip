@@ -16,18 +16,24 @@
 //   quant_act   int8 per 32-block of every token (+ H32), shared by all experts
 //   router/topk fp64 logits, top-k, softmax (the decode router's kernels)
 //   k_count     one workgroup per expert: number of pairs routed to it (16-byte reads)
-//   k_scan      expert offsets and the tile list (expert, first pair) of 64-pair tiles
+//   k_scan      expert offsets; the tile list (expert, first pair) of 64-pair
+//               tiles of the experts with more than small_pairs pairs, and the
+//               list of the experts with 1 .. small_pairs pairs (small_pairs: an
+//               argument of qmoe_prefill_layer_ex, 0 .. 4)
 //   k_scatter   one workgroup per expert: its pairs (t*K + s) in ascending order
-//   k_gateup    per (tile, 64 rows): int8 MFMA 16x16x32 per 32-block, so every
-//               MFMA result is one block's exact int32 sum; fp32 scale epilogue
-//               (weight scale x activation scale) per block; SwiGLU; the 64 x 64
+//   k_gateup    per (tile, 128 rows): int8 MFMA 32x32x32 per 32-block, so every
+//               MFMA result is one block's exact int32 sums; fp32 scale epilogue
+//               (weight scale x activation scale) per block; SwiGLU; the 128 x 64
 //               result is requantized per (pair, 32-row block) (+ H32) into hq
-//   k_down      per (tile, 64 rows): the same on the down weights and hq; the
+//   k_down      per (tile, 128 rows): the same on the down weights and hq; the
 //               routing weight is applied and each pair's row stored in ypair
+//   small path  the listed experts' pairs through the q <= 4 matvec arithmetic
+//               (sdot4 on byte-permuted codes, qmoe_decode.hip): a tile of one to
+//               four pairs would be mostly padding on the matrix cores
 //   k_combine   out[t] = sum over slots s = 0..K-1 (ascending expert id) of
 //               ypair[t][s]: a fixed order, so results are bit-reproducible.
 // The per-pair results do not depend on a pair's position inside a tile (MFMA
-// columns are independent), so the grouping affects speed only.
+// columns are independent), so the grouping within a path affects speed only.
 #include <hip/hip_runtime.h>
 
 #include "qmoe_device.h"
@@ -47,13 +53,16 @@ constexpr int kTileM = 128;  // weight rows per matrix and workgroup (4 waves x 
 constexpr int kKB = 8;       // 32-blocks per LDS stage (K = 256)
 
 // Group region (int32 words): counts[E], offsets[E+1], ntiles at 2E+1 (one word
-// of the cursor area), pairs[T*K] from word 3E+1, tiles (expert, first) after.
+// of the cursor area), pairs[T*K] from word 3E+1, tiles (expert, first) after
+// (room for T*K + E of them), then nsmall and the small-expert list [E].
 struct GroupPtrs {
   int32_t* counts;
   int32_t* offsets;
   int32_t* ntiles;
   int32_t* pairs;
   int32_t* tiles;
+  int32_t* nsmall;
+  int32_t* small;
 };
 
 GroupPtrs group_ptrs(uint8_t* g, int E, int npairs) {
@@ -64,6 +73,8 @@ GroupPtrs group_ptrs(uint8_t* g, int E, int npairs) {
   p.ntiles = w + 2 * E + 1;
   p.pairs = w + 3 * E + 1;
   p.tiles = w + 3 * E + 1 + npairs;
+  p.nsmall = p.tiles + 2 * (npairs + E);
+  p.small = p.nsmall + 1;
   return p;
 }
 
@@ -109,22 +120,28 @@ __global__ __launch_bounds__(256) void k_count(const int32_t* __restrict__ idx, 
   if (threadIdx.x == 0) counts[e] = c;
 }
 
-// One workgroup of 512 threads (E <= 512): exclusive scans of the counts and of
-// the per-expert tile counts, then the tile list.
-__global__ __launch_bounds__(512) void k_scan(const int32_t* __restrict__ counts, int E, int npairs,
-                                              int32_t* offsets, int32_t* ntiles, int32_t* tiles) {
-  __shared__ int s_c[512], s_t[512];
+// One workgroup of 512 threads (E <= 512): exclusive scans of the counts, of
+// the per-expert tile counts (experts with more than small_max pairs) and of
+// the small-expert flags (1 .. small_max pairs), then the tile list and the
+// small list.
+__global__ __launch_bounds__(512) void k_scan(const int32_t* __restrict__ counts, int E, int npairs, int small_max,
+                                              int32_t* offsets, int32_t* ntiles, int32_t* tiles, int32_t* nsmall,
+                                              int32_t* small) {
+  __shared__ int s_c[512], s_t[512], s_s[512];
   const int e = threadIdx.x;
   const int c = (e < E) ? counts[e] : 0;
-  const int t = (c + kTileN - 1) / kTileN;
+  const int sm = (c >= 1 && c <= small_max) ? 1 : 0;
+  const int t = sm ? 0 : (c + kTileN - 1) / kTileN;
   s_c[e] = c;
   s_t[e] = t;
+  s_s[e] = sm;
   __syncthreads();
   for (int o = 1; o < 512; o <<= 1) {   // inclusive Hillis-Steele scan
-    const int vc = (e >= o) ? s_c[e - o] : 0, vt = (e >= o) ? s_t[e - o] : 0;
+    const int vc = (e >= o) ? s_c[e - o] : 0, vt = (e >= o) ? s_t[e - o] : 0, vs = (e >= o) ? s_s[e - o] : 0;
     __syncthreads();
     s_c[e] += vc;
     s_t[e] += vt;
+    s_s[e] += vs;
     __syncthreads();
   }
   const int off = s_c[e] - c, toff = s_t[e] - t;
@@ -132,11 +149,13 @@ __global__ __launch_bounds__(512) void k_scan(const int32_t* __restrict__ counts
   if (e == 0) {
     offsets[E] = npairs;
     *ntiles = s_t[511];
+    *nsmall = s_s[511];
   }
   for (int i = 0; i < t; ++i) {
     tiles[2 * (toff + i)] = e;
     tiles[2 * (toff + i) + 1] = i * kTileN;
   }
+  if (sm) small[s_s[e] - 1] = e;
 }
 
 // Workgroup e writes the pairs routed to expert e in ascending order. With a
@@ -723,7 +742,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ypair
 }
 
 template <int FG, int FD>
-int launch_gemms(const PrefillArgs& a, int tiles_max, int ntok, float* out, hipStream_t s) {
+int launch_gemms(const PrefillArgs& a, const PrefillSmall& sp, int tiles_max, int ntok, float* out, hipStream_t s) {
   {
     launch_kernel("gateup_mfma", k_gateup<FG>, dim3(a.inter / kTileM, tiles_max), dim3(256), s, a);
   }
@@ -733,6 +752,7 @@ int launch_gemms(const PrefillArgs& a, int tiles_max, int ntok, float* out, hipS
     launch_kernel("down_mfma", k_down<FD>, dim3(a.hidden / kTileM, tiles_max), dim3(256), s, a);
   }
   if ((st = launch_check("down_mfma"))) return st;
+  if ((st = launch_prefill_small(sp, s))) return st;
   {
     const size_t n4 = (size_t)ntok * a.hidden / 4;
     const unsigned grid = (unsigned)std::min<size_t>((n4 + 255) / 256, 8192);
@@ -782,10 +802,11 @@ __global__ __launch_bounds__(256) void k_block_dots_mfma(const uint8_t* __restri
 }
 
 template <int FG>
-int launch_gemms_g(const PrefillArgs& a, int fd, int tiles_max, int ntok, float* out, hipStream_t s) {
-  if (fd == 2) return launch_gemms<FG, 2>(a, tiles_max, ntok, out, s);
-  if (fd == 3) return launch_gemms<FG, 3>(a, tiles_max, ntok, out, s);
-  return launch_gemms<FG, 4>(a, tiles_max, ntok, out, s);
+int launch_gemms_g(const PrefillArgs& a, const PrefillSmall& sp, int fd, int tiles_max, int ntok, float* out,
+                   hipStream_t s) {
+  if (fd == 2) return launch_gemms<FG, 2>(a, sp, tiles_max, ntok, out, s);
+  if (fd == 3) return launch_gemms<FG, 3>(a, sp, tiles_max, ntok, out, s);
+  return launch_gemms<FG, 4>(a, sp, tiles_max, ntok, out, s);
 }
 
 }  // namespace
@@ -821,8 +842,15 @@ extern "C" int qmoe_block_dots_mfma(int fmt, int64_t rows, int64_t k, const void
 
 extern "C" int qmoe_prefill_layer(const qmoe_layer* L, const float* x, int32_t ntok, float* out, void* ws,
                                   size_t ws_bytes, void* stream) {
+  return qmoe_prefill_layer_ex(L, x, ntok, out, ws, ws_bytes, QMOE_PREFILL_SMALL_DEFAULT, stream);
+}
+
+extern "C" int qmoe_prefill_layer_ex(const qmoe_layer* L, const float* x, int32_t ntok, float* out, void* ws,
+                                     size_t ws_bytes, int32_t small_pairs, void* stream) {
   clear_error();
   if (ntok < 0) QMOE_FAIL(QMOE_E_SHAPE, "ntok=%d must be >= 0", ntok);
+  if (small_pairs < 0 || small_pairs > kPrefillSmallPairs)
+    QMOE_FAIL(QMOE_E_INVAL, "small_pairs=%d outside 0..%d", small_pairs, kPrefillSmallPairs);
   WsPtrs w;
   int st = ws_ptrs(L, ntok > 0 ? ntok : 1, ws, ws_bytes, &w);
   if (st) return st;
@@ -841,8 +869,8 @@ extern "C" int qmoe_prefill_layer(const qmoe_layer* L, const float* x, int32_t n
   GroupPtrs g = group_ptrs(w.group, E, npairs);
   {
     launch_kernel("group_count", k_count, dim3(E), dim3(256), s, (const int32_t*)w.idx, npairs, g.counts);
-    launch_kernel("group_scan", k_scan, dim3(1), dim3(512), s, (const int32_t*)g.counts, E, npairs, g.offsets, g.ntiles,
-                  g.tiles);
+    launch_kernel("group_scan", k_scan, dim3(1), dim3(512), s, (const int32_t*)g.counts, E, npairs,
+                  (int)small_pairs, g.offsets, g.ntiles, g.tiles, g.nsmall, g.small);
     launch_kernel("group_scatter", k_scatter, dim3(E), dim3(256), s, (const int32_t*)w.idx, npairs,
                   (const int32_t*)g.offsets, g.pairs);
   }
@@ -878,10 +906,23 @@ extern "C" int qmoe_prefill_layer(const qmoe_layer* L, const float* x, int32_t n
   a.gu_stride = a.gu_row_bytes * L->inter;
   a.dn_row_bytes = (size_t)a.nb_i * fd.block_bytes;
   a.dn_stride = a.dn_row_bytes * L->hidden;
+  PrefillSmall sp{};
+  sp.L = L;
+  sp.xq = w.xq;
+  sp.dx = w.dx;
+  sp.counts = g.counts;
+  sp.offsets = g.offsets;
+  sp.pairs = g.pairs;
+  sp.nsmall = g.nsmall;
+  sp.small = g.small;
+  sp.gw = w.gw;
+  sp.hq = w.hq;
+  sp.dh = w.dh;
+  sp.ypair = w.ypair;
   const int tiles_max = max_tiles(npairs, E);
   switch (L->fmt_gate) {
-    case 2: return launch_gemms_g<2>(a, L->fmt_down, tiles_max, ntok, out, s);
-    case 3: return launch_gemms_g<3>(a, L->fmt_down, tiles_max, ntok, out, s);
-    default: return launch_gemms_g<4>(a, L->fmt_down, tiles_max, ntok, out, s);
+    case 2: return launch_gemms_g<2>(a, sp, L->fmt_down, tiles_max, ntok, out, s);
+    case 3: return launch_gemms_g<3>(a, sp, L->fmt_down, tiles_max, ntok, out, s);
+    default: return launch_gemms_g<4>(a, sp, L->fmt_down, tiles_max, ntok, out, s);
   }
 }

@@ -175,9 +175,31 @@ int qmoe_decode_layer_noalloc(const qmoe_layer* L, const float* x, int32_t q, fl
  * ([evox3] ladder: layer-major prefill batching). x: fp32 [ntok][hidden];
  * out: fp32 [ntok][hidden]. Deterministic: per token the expert outputs are
  * combined in ascending expert id. hidden and inter must be multiples of 256
- * (the GEMM tiles: 128 rows, K in stages of 256), else QMOE_E_SHAPE. */
+ * (the GEMM tiles: 128 rows, K in stages of 256), else QMOE_E_SHAPE.
+ * Experts are multiplied in 64-pair tiles on the int8 matrix cores; experts
+ * with at most QMOE_PREFILL_SMALL_DEFAULT pairs in the batch take the matvec
+ * path instead (see qmoe_prefill_layer_ex). */
 int qmoe_prefill_layer(const qmoe_layer* L, const float* x, int32_t ntok, float* out,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* qmoe_prefill_layer with the expert split as an argument: experts that 1 ..
+ * small_pairs (0..4) pairs of the batch route to go through the decode path's
+ * matvec arithmetic (each block expanded once by byte permutes, sdot4 against
+ * every pair) instead of a 64-pair MFMA tile that would be mostly padding
+ * ([evox3] ladder: the multi-token expert path next to the layer-major batch).
+ * 0 sends every expert to the tiles. The default (2) was the best or near it
+ * over batches of 32 .. 8192 tokens on MI355X, with and without Zipf-skewed
+ * routing: where every expert gets a handful of pairs the matvec path is up to
+ * 18% faster, at 8K it is within the run-to-run spread (the MFMA GEMMs are
+ * vector-ALU bound, so a padded tile's weight stream costs little there).
+ * Within a path a pair's result does not
+ * depend on the other tokens of the batch; the two paths round differently, so
+ * a token whose expert changes path between two batches can differ in the last
+ * bits (both within the layer's parity bar). small_pairs outside 0..4:
+ * QMOE_E_INVAL; other arguments and errors as qmoe_prefill_layer. */
+#define QMOE_PREFILL_SMALL_DEFAULT 2
+int qmoe_prefill_layer_ex(const qmoe_layer* L, const float* x, int32_t ntok, float* out,
+                          void* ws, size_t ws_bytes, int32_t small_pairs, void* stream);
 
 /* Expand-then-multiply form of qmoe_matvec, the comparison path for the fused
  * kernel ([0731-Strix], section "Lucebox Engine integration with Geometric":

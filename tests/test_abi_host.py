@@ -43,6 +43,12 @@ def test_every_declared_symbol_is_exported():
     assert set(B.EXPORTED) == set(names)
 
 
+def test_prefill_small_default_matches_header():
+    hdr = open(HEADER).read()
+    m = re.search(r"#define QMOE_PREFILL_SMALL_DEFAULT (\d+)", hdr)
+    assert m and int(m.group(1)) == qm.PREFILL_SMALL_DEFAULT
+
+
 def test_block_and_packed_bytes():
     assert [qm.qmoe_block_bytes(f) for f in (2, 3, 4)] == [10, 14, 17]
     assert qm.qmoe_block_bytes(5) == 0
