@@ -403,27 +403,51 @@ def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
         res["prefill_8k"] = {"status": f"not run: {e}"}
 
     # ---------------------------------------------------------------- dense FP4 + FP3/H32 mix
+    # one qmoe_matvec_group call (two launches: both inputs quantized, then both
+    # matrices' rows), and as the ablation one qmoe_matvec per matrix (three
+    # launches: the 16384-long input is quantized in a launch of its own)
     for ncols in (1, 4):
         fp4, fp3 = gen.dense_mix(ncols, seed=0)
         mats = [qm.device.DeviceMatrix(c) for c in (fp4, fp3)]
         xs = [torch.from_numpy(c.x).to(dev) for c in (fp4, fp3)]
         ys = [torch.empty((ncols, c.rows), dtype=torch.float32, device=dev) for c in (fp4, fp3)]
         wss = [m.workspace(ncols) for m in mats]
+        items = [(c.fmt, c.rows, c.k, m.w, m.cb, c.rot, x, y) for c, m, x, y in zip((fp4, fp3), mats, xs, ys)]
+        arr = qm.matvec_items(items)   # marshalled once: the timed loop is the C call alone
+        gws = torch.empty(qm.qmoe_matvec_group_workspace_bytes(items, ncols), dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream().cuda_stream
 
         def step():
+            st = qm.LIB.qmoe_matvec_group(arr, len(items), ncols, gws.data_ptr(), gws.numel(), stream)
+            if st:
+                raise qm.QmoeError(st, "qmoe_matvec_group", qm.LIB.qmoe_last_error().decode())
+
+        def step_per_matrix():
             for m, c, x, y, w in zip(mats, (fp4, fp3), xs, ys, wss):
                 qm.qmoe_matvec(c.fmt, c.rows, c.k, m.w, m.cb, c.rot, x, y, w)
-        for _ in range(10):
-            step()
-        with Timer(torch) as t:
-            for _ in range(K):
-                step()
-        ms = t.ms / K
         nbytes = sum(m.w.numel() for m in mats)
+        out = {}
+        for name, f in (("group", step), ("per_matrix", step_per_matrix)):
+            for _ in range(10):
+                f()
+            with Timer(torch) as t:
+                for _ in range(K):
+                    f()
+            out[name] = t.ms / K
+        ms = out["group"]
         gbs = nbytes / (ms * 1e-3) / 1e9
+        qm.qmoe_timing_enable(True)
+        for _ in range(K):
+            step()
+        torch.cuda.synchronize()
+        kern = {n: round(kernel_avg_ms(qm, n)[0] * 1e3, 2) for n in ("group_quant", "group_mv")}
+        qm.qmoe_timing_enable(False)
         res[f"dense_mix_q{ncols}"] = {"us_per_step": round(ms * 1e3, 2), "effective_GBps": round(gbs, 1),
-                                      "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "packed_bytes": nbytes}
-        log(f"dense mix q={ncols}: {ms * 1e3:.2f} us, {gbs:.1f} GB/s")
+                                      "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "packed_bytes": nbytes,
+                                      "kernel_us": kern, "entry_point": "qmoe_matvec_group",
+                                      "per_matrix_calls_us": round(out["per_matrix"] * 1e3, 2)}
+        log(f"dense mix q={ncols}: {ms * 1e3:.2f} us, {gbs:.1f} GB/s (one qmoe_matvec per matrix: "
+            f"{out['per_matrix'] * 1e3:.2f} us); kernels (us): " + ", ".join(f"{k}={v}" for k, v in kern.items()))
 
     # ---------------------------------------------------------------- fused versus expand-then-multiply
     fp3_big = gen.matvec_case(3, 4096, 16384, ncols=1, seed=0, rot=1)

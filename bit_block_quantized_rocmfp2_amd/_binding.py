@@ -42,6 +42,13 @@ class qmoe_layer(ctypes.Structure):
     ]
 
 
+class qmoe_matvec_item(ctypes.Structure):
+    _fields_ = [
+        ("fmt", c_int32), ("rot", c_int32), ("rows", c_int64), ("k", c_int64),
+        ("w", c_void_p), ("w_bytes", c_size_t), ("cb", c_void_p), ("x", c_void_p), ("y", c_void_p),
+    ]
+
+
 class qmoe_ws_layout(ctypes.Structure):
     _fields_ = [(n, c_size_t) for n in
                 ("xq", "dx", "idx", "gw", "logits", "plan", "hq", "dh", "group", "ypair", "total")]
@@ -80,6 +87,8 @@ def _load():
         "qmoe_prefill_layer_ex": (c_int, [POINTER(qmoe_layer), c_void_p, c_int32, c_void_p, c_void_p, c_size_t,
                                           c_int32, c_void_p]),
         "qmoe_matvec_workspace_bytes": (c_size_t, [c_int64, c_int32]),
+        "qmoe_matvec_group_workspace_bytes": (c_size_t, [POINTER(qmoe_matvec_item), c_int32, c_int32]),
+        "qmoe_matvec_group": (c_int, [POINTER(qmoe_matvec_item), c_int32, c_int32, c_void_p, c_size_t, c_void_p]),
         "qmoe_matvec": (c_int, [c_int, c_int64, c_int64, c_void_p, c_size_t, c_void_p, c_int32, c_void_p, c_int32,
                                 c_void_p, c_void_p, c_size_t, c_void_p]),
         "qmoe_matvec_expanded_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int32]),
@@ -112,7 +121,7 @@ EXPORTED = (
     "qmoe_strerror", "qmoe_last_error", "qmoe_version", "qmoe_block_bytes", "qmoe_packed_bytes", "qmoe_pack",
     "qmoe_unpack", "qmoe_layer_check", "qmoe_workspace_bytes", "qmoe_workspace_layout", "qmoe_route",
     "qmoe_decode_layer", "qmoe_decode_noalloc_max_bytes", "qmoe_decode_layer_noalloc", "qmoe_prefill_layer", "qmoe_prefill_layer_ex",
-    "qmoe_matvec_workspace_bytes", "qmoe_matvec", "qmoe_quant_act",
+    "qmoe_matvec_workspace_bytes", "qmoe_matvec_group_workspace_bytes", "qmoe_matvec_group", "qmoe_matvec", "qmoe_quant_act",
     "qmoe_block_dots", "qmoe_block_dots_mfma", "qmoe_matvec_expanded_workspace_bytes", "qmoe_matvec_expanded",
     "qmoe_quantize_workspace_bytes", "qmoe_quantize", "qmoe_timing_enable", "qmoe_timing_read", "qmoe_probe_read",
     "qmoe_probe_mfma", "qmoe_probe_valu",
@@ -244,6 +253,28 @@ PREFILL_SMALL_DEFAULT = 2
 def qmoe_prefill_layer_ex(L, x, out, ws, small_pairs, stream=None) -> None:
     _check(LIB.qmoe_prefill_layer_ex(ctypes.byref(L), _ptr(x), x.shape[0], _ptr(out), _ptr(ws), _nbytes(ws),
                                      small_pairs, _stream(stream)), "qmoe_prefill_layer_ex")
+
+
+def matvec_items(items):
+    """ctypes array of qmoe_matvec_item from (fmt, rows, k, w, cb, rot, x, y) tuples."""
+    arr = (qmoe_matvec_item * len(items))()
+    for a, (fmt, rows, k, w, cb, rot, x, y) in zip(arr, items):
+        a.fmt, a.rot, a.rows, a.k = fmt, rot, rows, k
+        a.w, a.w_bytes, a.cb, a.x, a.y = _ptr(w), _nbytes(w), _ptr(cb), _ptr(x), _ptr(y)
+    return arr
+
+
+def qmoe_matvec_group_workspace_bytes(items, ncols: int) -> int:
+    arr = matvec_items(items)
+    return LIB.qmoe_matvec_group_workspace_bytes(arr, len(items), ncols)
+
+
+def qmoe_matvec_group(items, ncols, ws, stream=None) -> None:
+    """items: (fmt, rows, k, w, cb, rot, x, y) per matrix (device tensors). The
+    first 16 bytes of ws must be zero before its first use (torch.zeros)."""
+    arr = matvec_items(items)
+    _check(LIB.qmoe_matvec_group(arr, len(items), ncols, _ptr(ws), _nbytes(ws), _stream(stream)),
+           "qmoe_matvec_group")
 
 
 def qmoe_matvec(fmt, rows, k, w, cb, rot, x, y, ws, stream=None) -> None:

@@ -1,0 +1,252 @@
+// Several packed matrix-vector products in two launches (gfx950): the dense
+// projections of one decode step, for example a 4-bit 4096 x 16384 matrix and a
+// 3-bit 4096 x 2048 one with H32 on its input, instead of one launch per
+// matrix plus one per long input's quantization.
+//
+// Page citations:
+//   [Strix-284B] lucebox.com, "DeepSeek V4 Flash: 284B model, up to 32 tok/s on
+//     AMD Ryzen AI MAX+ 395", section "ROCmFPX: fitting 284B weights into 128 GB"
+//     (decode reads the packed blocks directly and is bound by memory traffic)
+//     and section "Decode: up to 32 tok/s" (the dense 4-bit weights of a step,
+//     decoded once for all of its columns).
+//   [evox3] soothill.io, "DeepSeek V4 Flash 0731 on evox3", table "The
+//     optimization ladder" (the fused H32 matrix-vector path).
+//
+//   k_group_quant  every input of every matrix, one 32-block per half-wave (the
+//                  same IEEE operations as qmoe_quant_act), into the workspace
+//   k_group_mv     every matrix's rows in one grid: each workgroup serves one
+//                  matrix, each wave one row unit (the rows that one wave
+//                  covers, 64 / lanes-per-row of them) at a time, in the lane
+//                  mapping and accumulation order of qmoe_matvec, so every
+//                  output equals qmoe_matvec's bit for bit.
+// Each launch costs a fixed ~3 us on MI355X; the two-launch form pays it twice
+// where one launch per matrix plus one per long input pays it three or more
+// times. (A one-launch form with a grid barrier between the quantization and
+// the products was measured slower: its products cannot start before the
+// barrier, so they no longer overlap the weight stream.)
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "qmoe_device.h"
+#include "qmoe_host.h"
+#include "qmoe_internal.h"
+
+using namespace qk;
+using namespace qmoe;
+
+namespace {
+
+constexpr int kGroupMax = 4;      // matrices per call
+constexpr int kGroupThreads = 256;
+
+template <int FMT>
+constexpr int group_nbl() { return FMT == 4 ? 1 : 2; }
+
+struct GroupItem {
+  const uint8_t* w;
+  const int8_t* cb;
+  const float* x;
+  float* y;
+  int8_t* xq;        // quantized input [Q][nb][32] (workspace)
+  float* dx;         // its block scales [Q][nb]
+  int64_t rows;
+  size_t row_bytes;
+  int nb, lpr_log2, fmt, rot;
+  int units;         // row units of 64 >> lpr_log2 rows
+  int wg0, nwg;      // the item's workgroups of k_group_mv: wg0 .. wg0 + nwg - 1
+  int blk0;          // first block of this item in the quantization order
+};
+
+struct GroupArgs {
+  GroupItem it[kGroupMax];
+  int n;
+  int nblk;          // blocks to quantize, all items
+};
+
+// Half-wave h of the grid quantizes block h of the concatenated inputs.
+__global__ __launch_bounds__(kGroupThreads) void k_group_quant(GroupArgs g) {
+  const int lane = threadIdx.x & 63, j = lane & 31;
+  const int B = (blockIdx.x * (kGroupThreads / 64) + (threadIdx.x >> 6)) * 2 + (lane >> 5);
+  int i = 0;
+#pragma unroll
+  for (int k = 1; k < kGroupMax; ++k)
+    if (k < g.n && B >= g.it[k].blk0) i = k;
+  const GroupItem& it = g.it[i];
+  const int local = min(B, g.nblk - 1) - it.blk0;   // column local / nb, block local % nb
+  const float v = it.x[(size_t)(local / it.nb) * it.nb * 32 + (size_t)(local % it.nb) * 32 + j];
+  float d;
+  const uint32_t packed = quant_block32_lanes(v, it.rot, &d);
+  if (B < g.nblk) {
+    if ((j & 3) == 0) *reinterpret_cast<uint32_t*>(it.xq + (size_t)local * 32 + j) = packed;
+    if (j == 0) it.dx[local] = d;
+  }
+}
+
+// Row units lw, lw + W, ... of one matrix (W: its waves). The row's chunks
+// are taken UF at a time (all their loads issued before the first product), UF
+// as qmoe_matvec picks it: 4 with one or two columns, 2 with more.
+template <int FMT, int Q>
+__device__ __forceinline__ void group_wave(const GroupItem& it, int lw) {
+  constexpr int NBL = group_nbl<FMT>(), UF = (Q <= 2) ? 4 : 2;
+  const int lane = threadIdx.x & 63;
+  const int lpr_log2 = it.lpr_log2, lpr = 1 << lpr_log2;
+  const int sub = lane >> lpr_log2, sl = lane & (lpr - 1);
+  const int rpw = 64 >> lpr_log2;
+  const int nb = it.nb, W = it.nwg * (kGroupThreads / 64);
+  uint32_t cb[4];
+  load_codebook<FMT>(it.cb, cb);
+  for (int u = lw; u < it.units; u += W) {
+    const int64_t row = (int64_t)u * rpw + sub;
+    const bool ok = row < it.rows;
+    const uint8_t* rp = it.w + (size_t)(ok ? row : it.rows - 1) * it.row_bytes;
+    float acc[Q];
+#pragma unroll
+    for (int t = 0; t < Q; ++t) acc[t] = 0.0f;
+    for (int c0 = 0; c0 < nb; c0 += UF * lpr * NBL) {
+      Blocks<FMT, NBL> bl[UF];
+      Acts<NBL> act[UF][Q];
+#pragma unroll
+      for (int c = 0; c < UF; ++c) {
+        const int bc = min(c0 + c * lpr * NBL + sl * NBL, nb - NBL);   // clamped into the row
+        bl[c].load(rp, nb, bc);
+#pragma unroll
+        for (int t = 0; t < Q; ++t) act[c][t].load(it.xq + (size_t)t * nb * 32, it.dx + (size_t)t * nb, bc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < UF; ++c) {
+        const int b = c0 + c * lpr * NBL + sl * NBL;
+        if (ok && b < nb) {
+#pragma unroll
+          for (int i = 0; i < NBL; ++i) {
+            uint32_t w[8];
+            bl[c].expand(i, cb, w);
+            const float s = bl[c].scale(i);
+#pragma unroll
+            for (int t = 0; t < Q; ++t) {
+              const int p = block_dot(w, act[c][t].q[i]);
+              acc[t] = fmaf((float)p, s * act[c][t].d[i], acc[t]);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < Q; ++t) {
+      const float v = group_sum(acc[t], lpr);
+      if (sl == 0 && ok) it.y[(size_t)t * it.rows + row] = v;
+    }
+  }
+}
+
+template <int Q>
+__global__ __launch_bounds__(kGroupThreads) void k_group_mv(GroupArgs g) {
+  int i = 0;
+#pragma unroll
+  for (int k = 1; k < kGroupMax; ++k)
+    if (k < g.n && (int)blockIdx.x >= g.it[k].wg0) i = k;
+  const GroupItem& it = g.it[i];
+  const int lw = ((int)blockIdx.x - it.wg0) * (kGroupThreads / 64) + (threadIdx.x >> 6);
+  switch (it.fmt) {   // uniform over the workgroup
+    case 2: group_wave<2, Q>(it, lw); break;
+    case 3: group_wave<3, Q>(it, lw); break;
+    default: group_wave<4, Q>(it, lw); break;
+  }
+}
+
+template <int Q>
+int launch_group(GroupArgs& g, hipStream_t s) {
+  const int wpg = kGroupThreads / 64;
+  int grid = 0;
+  for (int i = 0; i < g.n; ++i) {   // one row unit per wave
+    g.it[i].nwg = (g.it[i].units + wpg - 1) / wpg;
+    g.it[i].wg0 = grid;
+    grid += g.it[i].nwg;
+  }
+  const int qgrid = (g.nblk + 2 * wpg - 1) / (2 * wpg);
+  launch_kernel("group_quant", k_group_quant, dim3(qgrid), dim3(kGroupThreads), s, g);
+  int st = launch_check("group_quant");
+  if (st) return st;
+  launch_kernel("group_mv", k_group_mv<Q>, dim3(grid), dim3(kGroupThreads), s, g);
+  return launch_check("group_mv");
+}
+
+size_t group_ws_bytes(const qmoe_matvec_item* m, int32_t n, int32_t ncols) {
+  size_t t = 0;
+  for (int i = 0; i < n; ++i) {
+    t += round_up((size_t)ncols * (size_t)m[i].k, 256);
+    t += round_up((size_t)ncols * (size_t)(m[i].k / 32) * 4, 256);
+  }
+  return t;
+}
+
+}  // namespace
+
+extern "C" size_t qmoe_matvec_group_workspace_bytes(const qmoe_matvec_item* m, int32_t n, int32_t ncols) {
+  if (!m || n < 1 || n > kGroupMax || ncols < 1 || ncols > 4) return 0;
+  for (int i = 0; i < n; ++i)
+    if (m[i].k <= 0 || m[i].k % 32) return 0;
+  return group_ws_bytes(m, n, ncols);
+}
+
+extern "C" int qmoe_matvec_group(const qmoe_matvec_item* m, int32_t n, int32_t ncols, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  clear_error();
+  if (!m) QMOE_FAIL(QMOE_E_INVAL, "NULL item list");
+  if (n < 1 || n > kGroupMax) QMOE_FAIL(QMOE_E_SHAPE, "n=%d outside 1..%d", n, kGroupMax);
+  if (ncols < 1 || ncols > 4) QMOE_FAIL(QMOE_E_SHAPE, "ncols=%d outside 1..4", ncols);
+  GroupArgs g{};
+  g.n = n;
+  int64_t nblk = 0, wgs = 0;
+  for (int i = 0; i < n; ++i) {
+    FormatInfo fi;
+    int st = check_matrix(m[i].fmt, m[i].rows, m[i].k, m[i].w, m[i].w_bytes, m[i].cb, &fi);
+    if (st) return st;
+    if (m[i].rot != 0 && m[i].rot != 1) QMOE_FAIL(QMOE_E_FORMAT, "item %d: rot=%d unsupported (0 or 1)", i, m[i].rot);
+    if (!m[i].x || !m[i].y) QMOE_FAIL(QMOE_E_INVAL, "item %d: NULL x or y", i);
+    if (!aligned16(m[i].x)) QMOE_FAIL(QMOE_E_INVAL, "item %d: x not 16-byte aligned", i);
+    if (m[i].rows < 1 || m[i].rows > (int64_t)1 << 31)
+      QMOE_FAIL(QMOE_E_SHAPE, "item %d: rows=%lld outside 1..2^31", i, (long long)m[i].rows);
+    const int nb = (int)(m[i].k / 32);
+    const int nbl = m[i].fmt == QMOE_FP4 ? 1 : 2;
+    const int lpr = lanes_per_row(nb, nbl);
+    GroupItem& it = g.it[i];
+    it.w = static_cast<const uint8_t*>(m[i].w);
+    it.cb = m[i].cb;
+    it.x = m[i].x;
+    it.y = m[i].y;
+    it.rows = m[i].rows;
+    it.row_bytes = (size_t)nb * fi.block_bytes;
+    it.nb = nb;
+    it.lpr_log2 = ilog2(lpr);
+    it.fmt = m[i].fmt;
+    it.rot = m[i].rot;
+    const int rpw = 64 / lpr;
+    it.units = (int)((m[i].rows + rpw - 1) / rpw);
+    it.blk0 = (int)nblk;
+    nblk += (int64_t)ncols * nb;
+    wgs += (it.units + 3) / 4;
+  }
+  if (nblk > (int64_t)1 << 30 || wgs > 0x7FFFFFFF)
+    QMOE_FAIL(QMOE_E_SHAPE, "too many input blocks (%lld) or workgroups (%lld)", (long long)nblk, (long long)wgs);
+  g.nblk = (int)nblk;
+  const size_t need = group_ws_bytes(m, n, ncols);
+  if (!ws) QMOE_FAIL(QMOE_E_WORKSPACE, "missing workspace (NULL)");
+  if (!aligned16(ws)) QMOE_FAIL(QMOE_E_WORKSPACE, "workspace not 16-byte aligned");
+  if (ws_bytes < need) QMOE_FAIL(QMOE_E_WORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  for (int i = 0; i < n; ++i) {
+    g.it[i].xq = reinterpret_cast<int8_t*>(p);
+    p += round_up((size_t)ncols * (size_t)m[i].k, 256);
+    g.it[i].dx = reinterpret_cast<float*>(p);
+    p += round_up((size_t)ncols * (size_t)(m[i].k / 32) * 4, 256);
+  }
+  hipStream_t s = as_stream(stream);
+  switch (ncols) {
+    case 1: return launch_group<1>(g, s);
+    case 2: return launch_group<2>(g, s);
+    case 3: return launch_group<3>(g, s);
+    default: return launch_group<4>(g, s);
+  }
+}

@@ -215,6 +215,32 @@ int qmoe_matvec_expanded(int fmt, int64_t rows, int64_t k, const void* w, size_t
                          const int8_t* cb, int32_t rot, const float* x, int32_t ncols, float* y,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* One matrix of qmoe_matvec_group: arguments as qmoe_matvec's. */
+typedef struct {
+  int32_t fmt, rot;
+  int64_t rows, k;
+  const void* w; size_t w_bytes;
+  const int8_t* cb;
+  const float* x;   /* fp32 [ncols][k], 16-byte aligned */
+  float* y;         /* fp32 [ncols][rows] */
+} qmoe_matvec_item;
+
+/* The matrix-vector products of n (1..4) matrices with the same number of
+ * columns in two launches (all inputs quantized, then all rows multiplied):
+ * the dense projections of a decode step ([Strix-284B], decode section: the
+ * dense 4-bit weights of a step decoded once for all of its columns; [evox3],
+ * table "The optimization ladder": the fused H32 matrix-vector path), where
+ * one qmoe_matvec per matrix pays a launch per matrix and one more for each
+ * long input's quantization. Each y equals qmoe_matvec's output for the same
+ * item bit for bit. ws:
+ * qmoe_matvec_group_workspace_bytes bytes, 16-byte aligned, caller-owned,
+ * scratch after the call (it holds the quantized inputs, item after item, each
+ * as qmoe_matvec's workspace does). Errors before any launch: as qmoe_matvec
+ * per item, n or ncols outside their ranges (QMOE_E_SHAPE). */
+size_t qmoe_matvec_group_workspace_bytes(const qmoe_matvec_item* m, int32_t n, int32_t ncols);
+int qmoe_matvec_group(const qmoe_matvec_item* m, int32_t n, int32_t ncols, void* ws,
+                      size_t ws_bytes, void* stream);
+
 /* Workspace bytes of qmoe_matvec for K = k and ncols columns. */
 size_t qmoe_matvec_workspace_bytes(int64_t k, int32_t ncols);
 

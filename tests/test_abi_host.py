@@ -258,3 +258,27 @@ def test_quantize_rejects_bad_arguments_before_launch():
     assert call(n=70000, rows=1) == -2                     # more matrices than grid rows
     assert qm.qmoe_quantize_workspace_bytes(1, 4, 33) == 0
     assert qm.qmoe_quantize_workspace_bytes(2, 2048, 4096) >= 2 * 2048 * 4096 * 2
+
+
+def test_matvec_group_host_checks():
+    """Workspace sizing and argument checks of qmoe_matvec_group (host only:
+    every refused call returns before any launch)."""
+    c = gen.matvec_case(3, 64, 512, 2, seed=2, rot=1)
+    w = formats.pack(3, c.codes, c.scales)
+    cb = np.ascontiguousarray(c.cb)
+    x = np.ascontiguousarray(c.x)
+    y = np.zeros((2, 64), dtype=np.float32)
+    items = [(3, 64, 512, w, cb, 1, x, y)]
+    per = -(-2 * 512 // 256) * 256 + -(-2 * 16 * 4 // 256) * 256
+    assert qm.qmoe_matvec_group_workspace_bytes(items, 2) == per
+    assert qm.qmoe_matvec_group_workspace_bytes(items * 2, 2) == 2 * per
+    assert qm.qmoe_matvec_group_workspace_bytes(items * 5, 2) == 0
+    assert qm.qmoe_matvec_group_workspace_bytes(items, 5) == 0
+    ws = np.zeros(per, dtype=np.uint8)
+    for bad, n, ncols, code in ((items, 5, 2, -2), (items, 1, 0, -2), ([(7,) + items[0][1:]], 1, 2, -3),
+                                ([(3, 64, 500) + items[0][3:]], 1, 2, -2)):
+        arr = B.matvec_items(bad[:1] if n == 5 else bad)
+        st = B.LIB.qmoe_matvec_group(arr, n, ncols, ws.ctypes.data, ws.nbytes, None)
+        assert st == code, (n, ncols, st)
+    arr = B.matvec_items(items)
+    assert B.LIB.qmoe_matvec_group(arr, 1, 2, ws.ctypes.data, ws.nbytes - 1, None) == -6

@@ -1,0 +1,118 @@
+"""qmoe_matvec_group (several packed matrix-vector products in two launches)
+against qmoe_matvec, bit for bit, through the C ABI; qmoe_matvec itself is held
+to the oracle by test_gpu_parity.py, and one case here checks the oracle
+directly."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+import bit_block_quantized_rocmfp2_amd as qm  # noqa: E402
+from oracle import dots, moe  # noqa: E402
+from synth import gen  # noqa: E402
+
+
+def setup(cases, ncols):
+    mats = [qm.device.DeviceMatrix(c) for c in cases]
+    xs = [torch.from_numpy(np.ascontiguousarray(c.x[:ncols])).cuda() for c in cases]
+    ys = [torch.full((ncols, c.rows), float("nan"), dtype=torch.float32, device="cuda") for c in cases]
+    items = [(c.fmt, c.rows, c.k, m.w, m.cb, c.rot, x, y) for c, m, x, y in zip(cases, mats, xs, ys)]
+    return mats, xs, ys, items
+
+
+def reference(cases, mats, xs, ncols):
+    out = []
+    for c, m, x in zip(cases, mats, xs):
+        y = torch.empty((ncols, c.rows), dtype=torch.float32, device="cuda")
+        qm.qmoe_matvec(c.fmt, c.rows, c.k, m.w, m.cb, c.rot, x, y, m.workspace(ncols))
+        out.append(y)
+    torch.cuda.synchronize()
+    return [y.cpu().numpy() for y in out]
+
+
+def run_group(items, ncols, ws=None):
+    if ws is None:
+        ws = torch.full((qm.qmoe_matvec_group_workspace_bytes(items, ncols),), 0xA5, dtype=torch.uint8,
+                        device="cuda")   # stale contents: the workspace needs no clearing
+    qm.qmoe_matvec_group(items, ncols, ws)
+    torch.cuda.synchronize()
+    return ws
+
+
+@pytest.mark.parametrize("ncols", [1, 2, 4])
+def test_group_dense_mix_bit_exact(ncols):
+    """The dense decode mix: FP4 4096 x 16384 and FP3 4096 x 2048 with H32 on
+    its input, in one launch, equal to two qmoe_matvec calls bit for bit; a
+    second call on the same workspace gives the same bits."""
+    cases = gen.dense_mix(ncols, seed=3)
+    mats, xs, ys, items = setup(cases, ncols)
+    ref = reference(cases, mats, xs, ncols)
+    ws = run_group(items, ncols)
+    for y, r in zip(ys, ref):
+        assert np.array_equal(y.cpu().numpy(), r)
+    for y in ys:
+        y.fill_(float("nan"))
+    run_group(items, ncols, ws)
+    for y, r in zip(ys, ref):
+        assert np.array_equal(y.cpu().numpy(), r)
+
+
+@pytest.mark.parametrize("ncols", [1, 3])
+def test_group_formats_ragged(ncols):
+    """Three and four matrices of every format, rows that fill no whole wave or
+    workgroup, K from 256 to 16384 (one to eight chunks per row)."""
+    cases = [gen.matvec_case(2, 1000, 2048, 4, seed=5, rot=0),
+             gen.matvec_case(3, 77, 512, 4, seed=6, rot=1),
+             gen.matvec_case(4, 4099, 16384, 4, seed=7, rot=1),
+             gen.matvec_case(2, 3, 256, 4, seed=8, rot=1)]
+    for sub in (cases[:3], cases):
+        mats, xs, ys, items = setup(sub, ncols)
+        ref = reference(sub, mats, xs, ncols)
+        run_group(items, ncols)
+        for y, r in zip(ys, ref):
+            assert np.array_equal(y.cpu().numpy(), r)
+
+
+def test_group_oracle():
+    """One group against the oracle's matvec directly (and its quantized inputs,
+    which the group leaves in the workspace, bit-exact); then a larger group
+    on the same workspace."""
+    cases = [gen.matvec_case(3, 300, 512, 2, seed=9, rot=1), gen.matvec_case(4, 129, 1024, 2, seed=10, rot=0)]
+    mats, xs, ys, items = setup(cases, 2)
+    big = gen.dense_mix(2, seed=11)
+    mats2, xs2, ys2, items2 = setup(big, 2)
+    nbytes = max(qm.qmoe_matvec_group_workspace_bytes(it, 2) for it in (items, items2))
+    ws = run_group(items, 2, torch.full((nbytes,), 0x5A, dtype=torch.uint8, device="cuda"))
+    off = 0
+    for c, y in zip(cases, ys):
+        y_ref, xq_ref, _ = dots.matvec(c.fmt, c.codes, c.scales, c.cb, c.x[:2], c.rot)
+        assert moe.rel_l2(y.cpu().numpy(), y_ref) < 1e-3
+        xq = ws[off: off + 2 * c.k].cpu().numpy().view(np.int8).reshape(2, c.k)
+        assert np.array_equal(xq, xq_ref)
+        off += -(-2 * c.k // 256) * 256 + -(-2 * (c.k // 32) * 4 // 256) * 256
+    run_group(items2, 2, ws)
+    for y, r in zip(ys2, reference(big, mats2, xs2, 2)):
+        assert np.array_equal(y.cpu().numpy(), r)
+
+
+def test_group_long_rows_and_bad_arguments():
+    """K = 32768 (several passes of the row per unit) bit for bit; n, ncols and
+    formats outside their ranges refused before any launch."""
+    c = gen.matvec_case(4, 64, 32768, 1, seed=1)
+    mats, xs, ys, items = setup([c], 1)
+    ref = reference([c], mats, xs, 1)
+    run_group(items, 1)
+    assert np.array_equal(ys[0].cpu().numpy(), ref[0])
+    ws = torch.zeros(qm.qmoe_matvec_group_workspace_bytes(items, 1), dtype=torch.uint8, device="cuda")
+    with pytest.raises(qm.QmoeError) as e:
+        qm.qmoe_matvec_group(items * 5, 1, ws)
+    assert e.value.status == -2
+    with pytest.raises(qm.QmoeError) as e:
+        qm.qmoe_matvec_group(items, 5, ws)
+    assert e.value.status == -2
+    bad = [(7,) + items[0][1:]]
+    with pytest.raises(qm.QmoeError) as e:
+        qm.qmoe_matvec_group(bad, 1, ws)
+    assert e.value.status == -3
