@@ -15,6 +15,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqmoe.so")
+LIB_DEBUG_PATH = os.path.join(_HERE, "libqmoe_debug.so")   # launcher bounds checks compiled in
 
 QMOE_OK = 0
 FP2, FP3, FP4 = 2, 3, 4
@@ -54,7 +55,9 @@ class qmoe_ws_layout(ctypes.Structure):
                 ("xq", "dx", "idx", "gw", "logits", "plan", "hq", "dh", "group", "ypair", "total")]
 
 
-def _load():
+def load_library(path=None):
+    """The library at `path` (default libqmoe.so) with every entry point's
+    signature set: the bounds-checked build (LIB_DEBUG_PATH) loads the same way."""
     # When torch is present it must load its HIP runtime first: libqmoe then binds
     # to that already-loaded libamdhip64.so.7 instead of a second runtime copy,
     # so device pointers and streams from torch are valid in the library.
@@ -62,9 +65,10 @@ def _load():
         import torch  # noqa: F401
     except ImportError:
         pass
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"libqmoe is not built ({LIB_PATH} missing); run __graft_entry__.build()")
-    lib = ctypes.CDLL(LIB_PATH)
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError(f"libqmoe is not built ({path} missing); run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
     sig = {
         "qmoe_strerror": (c_char_p, [c_int]),
         "qmoe_last_error": (c_char_p, []),
@@ -115,7 +119,7 @@ def _load():
     return lib
 
 
-LIB = _load()
+LIB = load_library()
 
 EXPORTED = (
     "qmoe_strerror", "qmoe_last_error", "qmoe_version", "qmoe_block_bytes", "qmoe_packed_bytes", "qmoe_pack",

@@ -1055,6 +1055,9 @@ __global__ __launch_bounds__(256) void k_pf_down_small(SmallArgs sa) {
 template <int FG, int FD>
 int launch_small_t(const SmallArgs& sa, hipStream_t s) {
   const DecodeArgs& a = sa.d;
+  QMOE_BOUNDS((a.inter / 32 + kSmallGateupPasses - 1) / kSmallGateupPasses * kSmallGateupPasses * 32 >= a.inter,
+              "prefill small path: gate/up grid covers the rows");
+  QMOE_BOUNDS(a.dn_lpr_log2 >= 0 && a.dn_lpr_log2 <= 6, "prefill small path: down lanes per row");
   const int rb = a.inter / 32;
   launch_kernel("gateup_small", k_pf_gateup_small<FG>,
                 dim3((rb + kSmallGateupPasses - 1) / kSmallGateupPasses, a.E), dim3(512), s, sa);
@@ -1157,6 +1160,16 @@ extern "C" int qmoe_decode_layer(const qmoe_layer* L, const float* x, int32_t q,
   a.dn_lpr_log2 = ilog2(lanes_per_row(a.nb_i, L->fmt_down == QMOE_FP4 ? 1 : 2));
   a.quant_per_wg = 4 * q;   // blocks per token-quantization workgroup: one pass of its half-waves
   const int U_max = std::min(q * L->topk, L->n_experts);
+  {   // the extents the decode kernels address (slot = 4 u + t for plan slot u, column t)
+    const size_t maxslot = (size_t)(U_max - 1) * 4 + (q - 1);
+    QMOE_BOUNDS((size_t)q * a.hidden <= w.n_xq && (size_t)q * a.nb_h * 4 <= w.n_dx, "decode: quantized tokens");
+    QMOE_BOUNDS((size_t)q * a.E * 8 <= w.n_logits, "decode: logits");
+    QMOE_BOUNDS((size_t)q * a.K * 4 <= w.n_idx && (size_t)q * a.K * 4 <= w.n_gw, "decode: routing ids and weights");
+    QMOE_BOUNDS(U_max <= kPlanMax && (size_t)(kPlanWOff + 4 * kPlanMax) * 4 <= w.n_plan, "decode: plan");
+    QMOE_BOUNDS((maxslot + 1) * a.inter <= w.n_hq && (maxslot + 1) * a.nb_i * 4 <= w.n_dh,
+                "decode: requantized intermediate rows");
+    QMOE_BOUNDS(a.inter % 32 == 0 && 4 * (64 >> a.dn_lpr_log2) > 0, "decode: gate/up row blocks, down rows per group");
+  }
   hipStream_t s = as_stream(stream);
   switch (q) {
     case 1: return launch_decode_q<1>(a, U_max, L->fmt_gate, L->fmt_down, s);

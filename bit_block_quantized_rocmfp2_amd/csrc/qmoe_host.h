@@ -48,6 +48,8 @@ struct WsPtrs {
   float* dh;
   uint8_t* group;
   float* ypair;
+  // region sizes in bytes (up to the next region), for the debug bounds checks
+  size_t n_xq, n_dx, n_idx, n_gw, n_logits, n_plan, n_hq, n_dh, n_group, n_ypair;
 };
 
 int ws_ptrs(const qmoe_layer* L, int32_t ntok, void* ws, size_t ws_bytes, WsPtrs* p);

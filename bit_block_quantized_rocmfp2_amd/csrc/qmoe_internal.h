@@ -40,3 +40,20 @@ inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
     ::qmoe::set_error(__VA_ARGS__); \
     return (code);                 \
   } while (0)
+
+// Debug builds (-DQMOE_DEBUG_BOUNDS, libqmoe_debug.so): before each launch the
+// host checks that the extents its kernels address, worked out from their own
+// index formulas, fit the buffers and that the grids cover the rows; a failed
+// check returns QMOE_E_INVAL naming the extent, and nothing is launched.
+// Release builds compile the checks out.
+#ifdef QMOE_DEBUG_BOUNDS
+#define QMOE_BOUNDS(cond, what)                                                             \
+  do {                                                                                      \
+    if (!(cond)) QMOE_FAIL(QMOE_E_INVAL, "bounds check failed: %s (%s)", what, #cond);      \
+  } while (0)
+#else
+#define QMOE_BOUNDS(cond, what) \
+  do {                          \
+    (void)sizeof((cond));       \
+  } while (0)
+#endif

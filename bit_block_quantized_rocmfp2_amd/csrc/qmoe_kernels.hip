@@ -509,6 +509,16 @@ int ws_ptrs(const qmoe_layer* L, int32_t ntok, void* ws, size_t ws_bytes, WsPtrs
   p->dh = reinterpret_cast<float*>(b + lay.dh);
   p->group = b + lay.group;
   p->ypair = reinterpret_cast<float*>(b + lay.ypair);
+  p->n_xq = lay.dx - lay.xq;
+  p->n_dx = lay.idx - lay.dx;
+  p->n_idx = lay.gw - lay.idx;
+  p->n_gw = lay.logits - lay.gw;
+  p->n_logits = lay.plan - lay.logits;
+  p->n_plan = lay.hq - lay.plan;
+  p->n_hq = lay.dh - lay.hq;
+  p->n_dh = lay.group - lay.dh;
+  p->n_group = lay.ypair - lay.group;
+  p->n_ypair = lay.total - lay.ypair;
   return QMOE_OK;
 }
 
@@ -688,6 +698,15 @@ extern "C" int qmoe_matvec(int fmt, int64_t rows, int64_t k, const void* w, size
   const int lg = ilog2(lanes_per_row(nb, nbl));
   const size_t row_bytes = (size_t)nb * fi.block_bytes;
   const uint8_t* W = static_cast<const uint8_t*>(w);
+  {
+    const size_t rows_per_wg = 4 * (64 >> lg);
+    QMOE_BOUNDS((size_t)ncols * k <= round_up((size_t)ncols * k, 256) &&
+                    round_up((size_t)ncols * k, 256) + (size_t)ncols * nb * 4 <= ws_bytes,
+                "matvec: quantized columns and scales inside the workspace");
+    QMOE_BOUNDS(((size_t)rows + rows_per_wg - 1) / rows_per_wg * rows_per_wg >= (size_t)rows,
+                "matvec: grid covers the rows");
+    QMOE_BOUNDS(lg >= 0 && lg <= 6 && (nbl << lg) <= nb, "matvec: lanes per row within the row's blocks");
+  }
   if ((int64_t)ncols * nb <= kFqMaxBlocks) {   // one launch: quantization inside the matvec
     switch (fmt) {
       case 2: launch_matvec_fq_f<2>(ncols, W, rows, row_bytes, nb, lg, cb, x, rot, xq, dx, y, s); break;

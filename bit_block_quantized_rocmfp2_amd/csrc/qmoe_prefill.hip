@@ -864,6 +864,18 @@ extern "C" int qmoe_prefill_layer_ex(const qmoe_layer* L, const float* x, int32_
   hipStream_t s = as_stream(stream);
   const int E = L->n_experts, K = L->topk;
   const int npairs = ntok * K;
+  {   // the extents the prefill kernels address
+    const size_t np = (size_t)npairs, I = L->inter, H = L->hidden;
+    const size_t group_words = 3 * (size_t)E + 1 + np + 2 * (np + E) + 1 + E;
+    QMOE_BOUNDS((size_t)ntok * H <= w.n_xq && (size_t)ntok * (H / 32) * 4 <= w.n_dx, "prefill: quantized tokens");
+    QMOE_BOUNDS((size_t)ntok * E * 8 <= w.n_logits, "prefill: logits");
+    QMOE_BOUNDS(np * 4 <= w.n_idx && np * 4 <= w.n_gw, "prefill: routing ids and weights");
+    QMOE_BOUNDS(group_words * 4 <= w.n_group, "prefill: group region (counts, offsets, pairs, tiles, small list)");
+    QMOE_BOUNDS((size_t)max_tiles(npairs, E) <= np + E, "prefill: tile list inside its room");
+    QMOE_BOUNDS(np * I <= w.n_hq && np * (I / 32) * 4 <= w.n_dh, "prefill: requantized intermediate rows");
+    QMOE_BOUNDS(np * H * 4 <= w.n_ypair, "prefill: per-pair output rows");
+    QMOE_BOUNDS(I % kTileM == 0 && H % kTileM == 0, "prefill: GEMM row tiles cover the rows exactly");
+  }
   if ((st = launch_quant(x, (int64_t)ntok * (L->hidden / 32), L->rot_gateup, w.xq, w.dx, s))) return st;
   if ((st = launch_route(L, x, ntok, w.logits, w.idx, w.gw, s))) return st;
   GroupPtrs g = group_ptrs(w.group, E, npairs);
