@@ -49,13 +49,15 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="only the q=1 headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=32)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="before the benchmark, copy MIB MiB device-to-device once (a plain copy of known size, "
                          "for scaling memory-traffic counters)")
     ap.add_argument("--prefill-only", action="store_true", help="only the 8K-token prefill (for profiling)")
     ap.add_argument("--quantize-only", action="store_true", help="only the weight quantizer (for profiling)")
     ap.add_argument("--decode-q4-only", action="store_true", help="only the q=4 decode (for profiling)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the warm q=1 calls and their kernel times (for the kernel-trace profile)")
     ap.add_argument("--prefill-small-sweep", action="store_true",
                     help="only: prefill time against the small-expert threshold over batch sizes")
     return ap.parse_args()
@@ -149,6 +151,22 @@ def main():
     bytes_q1 = spec.topk * per_expert
     value = bytes_q1 / (ms * 1e-3) / 1e9
     log(f"decode q=1: {ms * 1e3:.2f} us/call, {value:.1f} GB/s effective")
+    if args.headline_only:
+        K_only = K
+
+        def kernel_times_only(names):
+            qm.qmoe_timing_enable(True)
+            for i in range(K_only):
+                decode_q1(i)
+            torch.cuda.synchronize()
+            kt = {name: kernel_avg_ms(qm, name)[0] for name in names}
+            qm.qmoe_timing_enable(False)
+            return kt
+        kern = kernel_times_only(("route", "gateup", "down"))
+        log("decode q=1 kernels (us): " + ", ".join(f"{k}={v * 1e3:.2f}" for k, v in kern.items()))
+        print(json.dumps({"decode_q1_us_per_call": round(ms * 1e3, 2),
+                          "kernel_us": {k: round(v * 1e3, 2) for k, v in kern.items()}}), flush=True)
+        return
     # per-call distribution: a pair of events around each of K back-to-back calls
     evk = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
@@ -327,12 +345,12 @@ def bench_q4(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
                         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "groups": len(groups), "kernel_us": kern}
     log(f"decode q=4: {ms * 1e3:.2f} us/call, U={np.mean(U):.2f}, {gbs:.1f} GB/s; kernels (us): "
         + ", ".join(f"{k}={v}" for k, v in kern.items()))
-    return res, groups, out
+    return res, groups, out, ms
 
 
 def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
     K = max(20, args.steps // 2)
-    res, groups, out = bench_q4(args, torch, qm, gen, spec, dl, ws, per_expert, dev)
+    res, groups, out, ms = bench_q4(args, torch, qm, gen, spec, dl, ws, per_expert, dev)
 
     # ablation: the same four columns decoded one call per column (each expert
     # block decoded once per routed column instead of once per group)
