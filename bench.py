@@ -826,17 +826,20 @@ def cpu_baseline(args, spec, dl, per_expert, extra):
     legs = {}
     # q = 1 decode: the headline layer and its rotating tokens
     L = moe.Layer(spec.hidden, spec.inter, spec.n_experts, spec.topk, dl.w_router_host, get)
-    x = gen.tokens(64, spec.hidden, seed=0, stream=7)[:n]
+    # the GPU headline rotates the first 64 of these tokens; the sample continues the same stream
+    x = gen.tokens(max(64, n), spec.hidden, seed=0, stream=7)[:n]
+    n = x.shape[0]
+    n1 = max(1, n // 8)
     prepare(L, x)
     dt = run_tokens(L, x, nt)
-    dt1 = run_tokens(L, x[: max(1, n // 4)], 1)
+    dt1 = run_tokens(L, x[:n1], 1)
     gbs = n * spec.topk * per_expert / dt / 1e9
-    gbs1 = max(1, n // 4) * spec.topk * per_expert / dt1 / 1e9
+    gbs1 = n1 * spec.topk * per_expert / dt1 / 1e9
     legs["decode_q1"] = {"GBps": round(gbs, 5), "threads": nt, "tokens": n, "s": round(dt, 2),
-                         "single_thread_GBps": round(gbs1, 5), "single_thread_tokens": max(1, n // 4),
+                         "single_thread_GBps": round(gbs1, 5), "single_thread_tokens": n1,
                          "single_thread_s": round(dt1, 2)}
     log(f"cpu oracle: decode q=1 {n} tokens on {nt} threads {dt:.1f}s ({gbs:.4f} GB/s); "
-        f"{max(1, n // 4)} tokens on 1 thread {dt1:.1f}s ({gbs1:.4f} GB/s)")
+        f"{n1} tokens on 1 thread {dt1:.1f}s ({gbs1:.4f} GB/s)")
     # q = 4 decode: two forced-overlap groups (each token independent)
     groups = [gen.q4_group(spec.hidden, seed=0, variant=v) for v in range(2)]
     xg = np.concatenate(groups)
