@@ -458,7 +458,11 @@ def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
         for _ in range(K):
             step()
         torch.cuda.synchronize()
-        kern = {n: round(kernel_avg_ms(qm, n)[0] * 1e3, 2) for n in ("group_quant", "group_mv")}
+        kern = {}
+        for n in ("group_fq", "group_quant", "group_mv"):   # one launch (group_fq) or two
+            avg, cnt = kernel_avg_ms(qm, n)
+            if cnt:
+                kern[n] = round(avg * 1e3, 2)
         qm.qmoe_timing_enable(False)
         res[f"dense_mix_q{ncols}"] = {"us_per_step": round(ms * 1e3, 2), "effective_GBps": round(gbs, 1),
                                       "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "packed_bytes": nbytes,

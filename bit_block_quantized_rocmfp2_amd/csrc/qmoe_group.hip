@@ -12,18 +12,21 @@
 //   [evox3] soothill.io, "DeepSeek V4 Flash 0731 on evox3", table "The
 //     optimization ladder" (the fused H32 matrix-vector path).
 //
-//   k_group_quant  every input of every matrix, one 32-block per half-wave (the
-//                  same IEEE operations as qmoe_quant_act), into the workspace
+//   k_group_fq     (one or two columns, inputs of at most 512 blocks) one
+//                  launch: every workgroup quantizes its matrix's input into
+//                  LDS, then multiplies its rows
+//   k_group_quant  otherwise, every input of every matrix, one 32-block per
+//                  half-wave (the same IEEE operations as qmoe_quant_act), into
+//                  the workspace, then
 //   k_group_mv     every matrix's rows in one grid: each workgroup serves one
 //                  matrix, each wave one row unit (the rows that one wave
 //                  covers, 64 / lanes-per-row of them) at a time, in the lane
 //                  mapping and accumulation order of qmoe_matvec, so every
-//                  output equals qmoe_matvec's bit for bit.
-// Each launch costs a fixed ~3 us on MI355X; the two-launch form pays it twice
-// where one launch per matrix plus one per long input pays it three or more
-// times. (A one-launch form with a grid barrier between the quantization and
-// the products was measured slower: its products cannot start before the
-// barrier, so they no longer overlap the weight stream.)
+//                  output equals qmoe_matvec's bit for bit (both forms).
+// Each launch costs a fixed ~3 us on MI355X. (A one-launch form with a grid
+// barrier between the quantization and the products was measured slower: its
+// products cannot start before the barrier, so they no longer overlap the
+// weight stream.)
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -42,6 +45,7 @@ constexpr int kGroupThreads = 256;
 
 template <int FMT>
 constexpr int group_nbl() { return FMT == 4 ? 1 : 2; }
+inline int group_nbl_rt(int fmt) { return fmt == 4 ? 1 : 2; }
 
 struct GroupItem {
   const uint8_t* w;
@@ -83,17 +87,19 @@ __global__ __launch_bounds__(kGroupThreads) void k_group_quant(GroupArgs g) {
   }
 }
 
-// Row units lw, lw + W, ... of one matrix (W: its waves). The row's chunks
-// are taken UF at a time (all their loads issued before the first product), UF
-// as qmoe_matvec picks it: 4 with one or two columns, 2 with more.
-template <int FMT, int Q>
-__device__ __forceinline__ void group_wave(const GroupItem& it, int lw) {
-  constexpr int NBL = group_nbl<FMT>(), UF = (Q <= 2) ? 4 : 2;
+// Row units lw, lw + W, ... of one matrix (W: its waves; WPG waves per
+// workgroup). The row's chunks are taken UF at a time (all their loads issued
+// before the first product), UF as qmoe_matvec picks it: 4 with one or two
+// columns, 2 with more. xq / dx: the quantized input, [Q][nb][32] and [Q][nb],
+// in the workspace or in LDS.
+template <int FMT, int Q, int WPG, int UF = (Q <= 2) ? 4 : 2>
+__device__ __forceinline__ void group_wave(const GroupItem& it, int lw, const int8_t* xq, const float* dx) {
+  constexpr int NBL = group_nbl<FMT>();
   const int lane = threadIdx.x & 63;
   const int lpr_log2 = it.lpr_log2, lpr = 1 << lpr_log2;
   const int sub = lane >> lpr_log2, sl = lane & (lpr - 1);
   const int rpw = 64 >> lpr_log2;
-  const int nb = it.nb, W = it.nwg * (kGroupThreads / 64);
+  const int nb = it.nb, W = it.nwg * WPG;
   uint32_t cb[4];
   load_codebook<FMT>(it.cb, cb);
   for (int u = lw; u < it.units; u += W) {
@@ -111,7 +117,7 @@ __device__ __forceinline__ void group_wave(const GroupItem& it, int lw) {
         const int bc = min(c0 + c * lpr * NBL + sl * NBL, nb - NBL);   // clamped into the row
         bl[c].load(rp, nb, bc);
 #pragma unroll
-        for (int t = 0; t < Q; ++t) act[c][t].load(it.xq + (size_t)t * nb * 32, it.dx + (size_t)t * nb, bc);
+        for (int t = 0; t < Q; ++t) act[c][t].load(xq + (size_t)t * nb * 32, dx + (size_t)t * nb, bc);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -148,21 +154,98 @@ __global__ __launch_bounds__(kGroupThreads) void k_group_mv(GroupArgs g) {
     if (k < g.n && (int)blockIdx.x >= g.it[k].wg0) i = k;
   const GroupItem& it = g.it[i];
   const int lw = ((int)blockIdx.x - it.wg0) * (kGroupThreads / 64) + (threadIdx.x >> 6);
+  constexpr int WPG = kGroupThreads / 64;
   switch (it.fmt) {   // uniform over the workgroup
-    case 2: group_wave<2, Q>(it, lw); break;
-    case 3: group_wave<3, Q>(it, lw); break;
-    default: group_wave<4, Q>(it, lw); break;
+    case 2: group_wave<2, Q, WPG>(it, lw, it.xq, it.dx); break;
+    case 3: group_wave<3, Q, WPG>(it, lw, it.xq, it.dx); break;
+    default: group_wave<4, Q, WPG>(it, lw, it.xq, it.dx); break;
+  }
+}
+
+// One-launch form, for one or two columns when every item's input holds at
+// most kFqMaxBlocks blocks (all columns): each workgroup first quantizes its
+// item's whole input into LDS, one block per thread with all 32 values in the
+// thread's registers (quant_block32: the same IEEE operations as
+// k_group_quant's half-waves, so the same bytes and scales), then, after one
+// barrier, runs the item's row units through group_wave from LDS. The item's
+// first workgroup also writes the quantized input to the workspace, as the
+// two-launch form does. Workgroups of 8 waves keep the redundant quantization
+// to one block per thread for a 16384-wide input, and at one column the
+// kernel fits three of them per compute unit. (Requesting each wave's first
+// row of weights before the quantization, so that the stream starts earlier,
+// measured slower: 13.8 against 12.7 us for the dense 4-bit 16384 + 3-bit 2048
+// pair; workgroups of 4 waves doubled the redundant quantization: 15.8 us.)
+constexpr int kFqThreads = 512;
+constexpr int kFqMaxBlocks = 512;
+constexpr int kFqUF = 2;   // chunks per step (the per-lane block order does not depend on it)
+
+template <int Q>
+__global__ __launch_bounds__(kFqThreads, Q == 1 ? 6 : 4) void k_group_fq(GroupArgs g) {
+  __shared__ u32x4 s_xq[2 * kFqMaxBlocks];
+  __shared__ float s_dx[kFqMaxBlocks];
+  int i = 0;
+#pragma unroll
+  for (int k = 1; k < kGroupMax; ++k)
+    if (k < g.n && (int)blockIdx.x >= g.it[k].wg0) i = k;
+  const GroupItem& it = g.it[i];
+  const int tid = threadIdx.x;
+  const bool first = (int)blockIdx.x == it.wg0;
+  // the item's input, one block per thread per pass (column B / nb, block B % nb)
+  for (int B = tid; B < Q * it.nb; B += kFqThreads) {
+    const float4* src = reinterpret_cast<const float4*>(it.x + (size_t)B * 32);
+    float v[32];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float4 f = src[k];
+      v[4 * k] = f.x; v[4 * k + 1] = f.y; v[4 * k + 2] = f.z; v[4 * k + 3] = f.w;
+    }
+    uint32_t q[8];
+    float d;
+    quant_block32(v, it.rot, q, &d);
+    const u32x4 lo = {q[0], q[1], q[2], q[3]}, hi = {q[4], q[5], q[6], q[7]};
+    s_xq[2 * B] = lo;
+    s_xq[2 * B + 1] = hi;
+    s_dx[B] = d;
+    if (first) {
+      reinterpret_cast<u32x4*>(it.xq)[2 * B] = lo;
+      reinterpret_cast<u32x4*>(it.xq)[2 * B + 1] = hi;
+      it.dx[B] = d;
+    }
+  }
+  __syncthreads();
+  constexpr int WPG = kFqThreads / 64;
+  const int lw = ((int)blockIdx.x - it.wg0) * WPG + (tid >> 6);
+  const int8_t* xq = reinterpret_cast<const int8_t*>(s_xq);
+  switch (it.fmt) {   // uniform over the workgroup
+    case 2: group_wave<2, Q, WPG, kFqUF>(it, lw, xq, s_dx); break;
+    case 3: group_wave<3, Q, WPG, kFqUF>(it, lw, xq, s_dx); break;
+    default: group_wave<4, Q, WPG, kFqUF>(it, lw, xq, s_dx); break;
   }
 }
 
 template <int Q>
 int launch_group(GroupArgs& g, hipStream_t s) {
-  const int wpg = kGroupThreads / 64;
+  bool fq = Q <= 2;   // (three or four columns do not fit the one-launch form's registers)
+  for (int i = 0; i < g.n; ++i) fq = fq && Q * g.it[i].nb <= kFqMaxBlocks;
+  const int wpg = (fq ? kFqThreads : kGroupThreads) / 64;
   int grid = 0;
   for (int i = 0; i < g.n; ++i) {   // one row unit per wave
     g.it[i].nwg = (g.it[i].units + wpg - 1) / wpg;
     g.it[i].wg0 = grid;
     grid += g.it[i].nwg;
+    // every row unit has a wave; the quantized input fits its workspace region
+    QMOE_BOUNDS((int64_t)g.it[i].nwg * wpg >= g.it[i].units &&
+                    (int64_t)g.it[i].units * (64 >> g.it[i].lpr_log2) >= g.it[i].rows,
+                "matvec group: grid covers the rows");
+    QMOE_BOUNDS(g.it[i].lpr_log2 >= 0 && g.it[i].lpr_log2 <= 6 &&
+                    (group_nbl_rt(g.it[i].fmt) << g.it[i].lpr_log2) <= g.it[i].nb,
+                "matvec group: lanes per row within the row");
+  }
+  if constexpr (Q <= 2) {
+    if (fq) {
+      launch_kernel("group_fq", k_group_fq<Q>, dim3(grid), dim3(kFqThreads), s, g);
+      return launch_check("group_fq");
+    }
   }
   const int qgrid = (g.nblk + 2 * wpg - 1) / (2 * wpg);
   launch_kernel("group_quant", k_group_quant, dim3(qgrid), dim3(kGroupThreads), s, g);

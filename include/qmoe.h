@@ -226,7 +226,10 @@ typedef struct {
 } qmoe_matvec_item;
 
 /* The matrix-vector products of n (1..4) matrices with the same number of
- * columns in two launches (all inputs quantized, then all rows multiplied):
+ * columns in one launch when ncols <= 2 and every input holds at most 512
+ * blocks per call (ncols x k / 32; each workgroup quantizes its matrix's input
+ * into LDS, then multiplies), else in two launches (all inputs quantized, then
+ * all rows multiplied):
  * the dense projections of a decode step ([Strix-284B], decode section: the
  * dense 4-bit weights of a step decoded once for all of its columns; [evox3],
  * table "The optimization ladder": the fused H32 matrix-vector path), where

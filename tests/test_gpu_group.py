@@ -116,3 +116,27 @@ def test_group_long_rows_and_bad_arguments():
     with pytest.raises(qm.QmoeError) as e:
         qm.qmoe_matvec_group(bad, 1, ws)
     assert e.value.status == -3
+
+
+@pytest.mark.parametrize("ncols,k,one_launch", [(1, 16384, True), (2, 8192, True), (2, 8448, False),
+                                                 (3, 2048, False)])
+def test_group_launch_forms(ncols, k, one_launch):
+    """The one-launch form (inputs quantized into LDS by every workgroup) runs
+    for one or two columns when each input holds at most 512 blocks, the
+    two-launch form otherwise; both equal qmoe_matvec bit for bit, and both
+    leave the quantized inputs in the workspace."""
+    cases = [gen.matvec_case(2, 200, k, 4, seed=20, rot=1), gen.matvec_case(3, 64, 2048, 4, seed=21, rot=0)]
+    mats, xs, ys, items = setup(cases, ncols)
+    ref = reference(cases, mats, xs, ncols)
+    qm.qmoe_timing_enable(True)
+    try:
+        ws = run_group(items, ncols)
+        ran = {n: qm.qmoe_timing_read(n)[1] for n in ("group_fq", "group_quant", "group_mv")}
+    finally:
+        qm.qmoe_timing_enable(False)
+    assert (ran["group_fq"] == 1) == one_launch and (ran["group_mv"] == 1) == (not one_launch), ran
+    for y, r in zip(ys, ref):
+        assert np.array_equal(y.cpu().numpy(), r)
+    c = cases[0]
+    _, xq_ref, _ = dots.matvec(c.fmt, c.codes, c.scales, c.cb, c.x[:ncols], c.rot)
+    assert np.array_equal(ws[: ncols * c.k].cpu().numpy().view(np.int8).reshape(ncols, c.k), xq_ref)
