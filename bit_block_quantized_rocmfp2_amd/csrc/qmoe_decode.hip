@@ -140,52 +140,31 @@ struct PlanLds {
   int ids[4][8];          // plan writer only: selected ids of token t, ascending
   float w[4][8];          // plan writer only: their routing weights
   int e;                  // one token: the expert of this workgroup's plan slot
+  int uid[kPlanMax];      // q > 1: plan slot s -> its expert (the s-th distinct id, ascending)
+  uint32_t umask[kPlanMax];  // q > 1: its column mask
+  int U;                  // q > 1: plan size
 };
+
+// Workgroup barrier that orders LDS accesses only: this wave's LDS operations
+// complete before it, and vector-memory loads in flight stay in flight across
+// it. (__syncthreads also waits for those.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // Every workgroup selects the experts itself. With one token wave 0 runs the
 // top-k and passes the expert of slot u (the plan is the K ids ascending with
-// column mask 1) to the other waves through LDS. With q > 1 tokens, waves t < q select token t and set its
-// experts in an LDS bitmap; after one barrier every wave reads the union of the
-// bitmaps: plan slot s holds the s-th set bit, i.e. the distinct ids in
-// ascending order, and its column mask is that bit across the tokens. Returns
-// the expert of plan slot u (-1 if u is beyond the plan) and its column mask.
-// `write` (one workgroup) also computes the routing weights and stores the
-// routing (idx, gw) and the plan (size, ids, masks, weights per column).
-// Plan slot u from the per-token bitmaps in LDS (q > 1): the u-th set bit of
-// their union, its column mask, the union word of lane l (l < words) and the
-// plan size U. Uniform across the workgroup.
-template <int Q>
-__device__ __forceinline__ int plan_slot(const DecodeArgs& a, const PlanLds& P, int u, uint32_t& mask,
-                                         uint32_t& uw, int& U) {
-  const int lane = threadIdx.x & 63;
-  const int nw = (a.E + 31) >> 5;
-  uw = 0;   // lane l < nw: word l of the union bitmap
-  if (lane < nw)
-#pragma unroll
-    for (int t = 0; t < Q; ++t)
-      if (t < a.q) uw |= P.bits[t][lane];
-  // slot u: uniform walk over the words
-  int e = -1, rem = u;
-  U = 0;
-  for (int w = 0; w < nw; ++w) {
-    const uint32_t word = (uint32_t)__builtin_amdgcn_readlane(uw, w);
-    const int c = __popc(word);
-    if (e < 0 && rem < c) {
-      uint32_t x = word;
-      for (int i = 0; i < rem; ++i) x &= x - 1;
-      e = 32 * w + (int)__builtin_ctz(x);
-    }
-    if (e < 0) rem -= c;
-    U += c;
-  }
-  mask = 0;
-  if (e >= 0)
-#pragma unroll
-    for (int t = 0; t < Q; ++t)
-      if (t < a.q && (P.bits[t][e >> 5] >> (e & 31) & 1u)) mask |= 1u << t;
-  return e;
-}
-
+// column mask 1) to the other waves through LDS. With q > 1 tokens, waves t < q
+// select token t and set its experts in an LDS bitmap; after one barrier wave 0
+// lists the union of the bitmaps in LDS: plan slot s holds the s-th set bit,
+// i.e. the distinct ids in ascending order, and its column mask is that bit
+// across the tokens (P.uid, P.umask, P.U, read by every item of the
+// workgroup). Returns the expert of plan slot u (-1 if u is beyond the plan)
+// and its column mask. `write` (one workgroup) also computes the routing
+// weights and stores the routing (idx, gw) and the plan (size, ids, masks,
+// weights per column).
 template <int Q>
 __device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, int u, bool write, uint32_t& mask,
                                              int* U_out = nullptr) {
@@ -214,8 +193,9 @@ __device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, in
     if (U_out) *U_out = a.K;
     return P.e;
   } else {
+    // (the barriers order LDS only: other waves' loads stay in flight across them)
     if (tid < 64) (&P.bits[0][0])[tid] = 0u;
-    __syncthreads();
+    lds_barrier();
     if (wave < a.q) {
       const uint64_t first = topk_select(a.logits + (size_t)wave * a.E, a.E, a.K, lane, p);
       if (lane < a.K) atomicOr(&P.bits[wave][p.id >> 5], 1u << (p.id & 31));
@@ -229,15 +209,18 @@ __device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, in
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
+    // wave 0 lists the plan once for the workgroup: lane s < U takes the s-th
+    // set bit of the union of the bitmaps (the distinct ids in ascending
+    // order) and its column mask; the items then read their slot from LDS
     const int nw = (a.E + 31) >> 5;
-    uint32_t uw;
-    int U;
-    const int e = plan_slot<Q>(a, P, u, mask, uw, U);
-    if (U_out) *U_out = U;
-    if (write && wave == 0) {
-      // lane s < U: the s-th distinct expert, its mask and weights
-      int es = -1, rs = lane;
+    if (wave == 0) {
+      uint32_t uw = 0;   // lane l < words: word l of the union bitmap
+      if (lane < nw)
+#pragma unroll
+        for (int t = 0; t < Q; ++t)
+          if (t < a.q) uw |= P.bits[t][lane];
+      int es = -1, rs = lane, Ucount = 0;
       for (int w = 0; w < nw; ++w) {
         const uint32_t word = (uint32_t)__builtin_amdgcn_readlane(uw, w);
         const int c = __popc(word);
@@ -247,15 +230,16 @@ __device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, in
           es = 32 * w + (int)__builtin_ctz(x);
         }
         if (es < 0) rs -= c;
+        Ucount += c;
       }
-      if (lane < kPlanMax) {
-        uint32_t ms = 0;
-        float4 ws = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (es >= 0)
+      uint32_t ms = 0;
+      float4 ws = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (lane < kPlanMax && es >= 0)
 #pragma unroll
-          for (int t = 0; t < Q; ++t)
-            if (t < a.q && (P.bits[t][es >> 5] >> (es & 31) & 1u)) {
-              ms |= 1u << t;
+        for (int t = 0; t < Q; ++t)
+          if (t < a.q && (P.bits[t][es >> 5] >> (es & 31) & 1u)) {
+            ms |= 1u << t;
+            if (write) {
               float wt = 0.0f;
 #pragma unroll
               for (int k = 0; k < 8; ++k)
@@ -265,12 +249,26 @@ __device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, in
               if (t == 2) ws.z = wt;
               if (t == 3) ws.w = wt;
             }
-        a.plan[kPlanIdOff + lane] = es;
-        a.plan[kPlanMaskOff + lane] = (int)ms;
-        reinterpret_cast<float4*>(a.plan + kPlanWOff)[lane] = ws;
+          }
+      if (lane < kPlanMax) {
+        P.uid[lane] = es;
+        P.umask[lane] = ms;
+        if (write) {
+          a.plan[kPlanIdOff + lane] = es;
+          a.plan[kPlanMaskOff + lane] = (int)ms;
+          reinterpret_cast<float4*>(a.plan + kPlanWOff)[lane] = ws;
+        }
       }
-      if (lane == 0) a.plan[0] = U;
+      if (lane == 0) {
+        P.U = Ucount;
+        if (write) a.plan[0] = Ucount;
+      }
     }
+    lds_barrier();
+    const int U = P.U;
+    if (U_out) *U_out = U;
+    const int e = (u < U) ? P.uid[u] : -1;
+    mask = (u < U) ? P.umask[u] : 0u;
     return e;
   }
 }
@@ -489,9 +487,8 @@ __global__ __launch_bounds__(512) void k_gateupq(DecodeArgs a) {
   const int nrb = a.inter / 32;
   for (int it = blockIdx.x; it < U * nrb; it += gridDim.x) {
     const int u = it / nrb;
-    uint32_t uw;
-    int Uu;
-    const int e = plan_slot<Q>(a, P, u, mask, uw, Uu);
+    const int e = P.uid[u];
+    mask = P.umask[u];
     gateup_item<FMT, Q>(a, e, mask, u, it % nrb, s_a);
     __syncthreads();   // s_a is reused by the next item
   }
@@ -515,17 +512,45 @@ __global__ __launch_bounds__(1024) void k_gateupq2(DecodeArgs a) {
   __shared__ u32x4 s_xq[Q * 256];   // per token: 64 lanes x CPL pieces
   __shared__ float s_dx[Q * 128];   // per token: 64 lanes x NBL scales
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nb = a.nb_h;
+  // The waves that do not select (wave >= Q) request the tokens' int8 blocks
+  // and scales before the selection, so those loads complete while waves
+  // 0 .. q-1 select (the selection's barriers order LDS only); the pieces are
+  // stored to LDS afterwards. Every load of a copying thread is issued (index
+  // clamped).
+  constexpr int NCP = 1024 - 64 * Q;                     // copying threads
+  constexpr int NXP = (Q * 256 + NCP - 1) / NCP;          // 16-byte pieces per copying thread
+  constexpr int NDP = (Q * 128 + NCP - 1) / NCP;          // scales per copying thread
+  const int ct = tid - 64 * Q;
+  const int npx = Q * nb * 2, npd = Q * nb;
+  u32x4 xv[NXP];
+  float dv[NDP];
+  if (ct >= 0) {   // (uniform per wave: the selecting waves issue nothing before their logits)
+#pragma unroll
+    for (int k = 0; k < NXP; ++k) xv[k] = reinterpret_cast<const u32x4*>(a.xq)[min(ct + NCP * k, npx - 1)];
+#pragma unroll
+    for (int k = 0; k < NDP; ++k) dv[k] = a.dx[min(ct + NCP * k, npd - 1)];
+  }
   uint32_t mask0;
   int U;
   topk_and_plan<Q>(a, P, 0, blockIdx.x == 0, mask0, &U);
-  const int nb = a.nb_h;
-  for (int i = tid; i < Q * nb * 2; i += 1024) {
-    const int t = i / (nb * 2), g = i % (nb * 2);
-    s_xq[t * 256 + (g % CPL) * 64 + g / CPL] = reinterpret_cast<const u32x4*>(a.xq)[i];
-  }
-  for (int i = tid; i < Q * nb; i += 1024) {
-    const int t = i / nb, k = i % nb;
-    s_dx[t * 128 + (k % NBL) * 64 + k / NBL] = a.dx[i];
+  if (ct >= 0) {
+#pragma unroll
+    for (int k = 0; k < NXP; ++k) {
+      const int i = ct + NCP * k;
+      if (i < npx) {
+        const int t = i / (nb * 2), g = i % (nb * 2);
+        s_xq[t * 256 + (g % CPL) * 64 + g / CPL] = xv[k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NDP; ++k) {
+      const int i = ct + NCP * k;
+      if (i < npd) {
+        const int t = i / nb, kk = i % nb;
+        s_dx[t * 128 + (kk % NBL) * 64 + kk / NBL] = dv[k];
+      }
+    }
   }
   __syncthreads();
   const int nrb = a.inter / 32;
@@ -534,9 +559,8 @@ __global__ __launch_bounds__(1024) void k_gateupq2(DecodeArgs a) {
   const int bc = min(b, nb - NBL);
   for (int it = blockIdx.x; it < U * nrb; it += gridDim.x) {
     const int u = it / nrb, rb = it % nrb;
-    uint32_t mask, uw;
-    int Uu;
-    const int e = plan_slot<Q>(a, P, u, mask, uw, Uu);
+    const uint32_t mask = P.umask[u];
+    const int e = P.uid[u];
     const int row0 = rb * 32 + wave * RPW;
     const uint8_t* gbase = a.gate + (size_t)e * a.gu_stride;
     const uint8_t* ubase = a.up + (size_t)e * a.gu_stride;
