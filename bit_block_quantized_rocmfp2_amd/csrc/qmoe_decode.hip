@@ -695,8 +695,12 @@ __global__ __launch_bounds__(256) void k_down(DecodeArgs a) {
 // (experts ascending, then columns, then the lane's blocks).
 constexpr int kDownqActPieces = 48 * 1024 / 16;   // 16-byte pieces of staged activations
 constexpr int kDownqMaxSlots = 32;
+// 8 waves per workgroup: one copy of the routed activations serves 8 waves'
+// rows (with 4 waves, the copies of all workgroups, re-read from the shared
+// cache levels, added 0.8x the weight bytes to the traffic of the launch)
+constexpr int kDownqThreads = 512;
 template <int FMT, int Q>
-__global__ __launch_bounds__(256) void k_downq(DecodeArgs a) {
+__global__ __launch_bounds__(kDownqThreads) void k_downq(DecodeArgs a) {
   constexpr int NBL = (FMT == 4) ? 1 : 2;
   constexpr int UB = 12;
   constexpr int CPL = 2 * NBL;   // 16-byte activation pieces per lane and slot
@@ -704,14 +708,15 @@ __global__ __launch_bounds__(256) void k_downq(DecodeArgs a) {
   const int lpr = 1 << lpr_log2;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int sub = lane >> lpr_log2, sl = lane & (lpr - 1);
-  const int row = (blockIdx.x * 4 + wave) * (64 >> lpr_log2) + sub;
+  const int row = (blockIdx.x * (kDownqThreads / 64) + wave) * (64 >> lpr_log2) + sub;
   __shared__ int s_plan[kPlanWOff + 4 * kPlanMax];
   __shared__ int s_slot[kDownqMaxSlots];      // compact slot c -> u * 4 + t
   __shared__ int s_cidx[4 * kPlanMax];        // u * 4 + t -> compact slot
   __shared__ int s_nslot;
-  __shared__ u32x4 s_act[kDownqActPieces + 256];
-  __shared__ u32x4 s_dh[kDownqMaxSlots * 16 + 256];
-  s_plan[tid] = a.plan[tid];
+  __shared__ u32x4 s_act[kDownqActPieces];
+  __shared__ u32x4 s_dh[kDownqMaxSlots * 16];
+  static_assert(kPlanWOff + 4 * kPlanMax == 256, "plan fits one load per thread of the first 256");
+  if (tid < 256) s_plan[tid] = a.plan[tid];
   __syncthreads();
   const int U = s_plan[0];
   const float* pw = reinterpret_cast<const float*>(s_plan + kPlanWOff);
@@ -750,19 +755,19 @@ __global__ __launch_bounds__(256) void k_downq(DecodeArgs a) {
   const int pps = nb * 2;   // pieces per slot (= lpr * CPL)
   const int nq = nslot * pps;
   const int nd = nslot * (nb / 4);   // 16-byte pieces of scales (4 per piece)
-  constexpr int AP = kDownqActPieces / 256;
-  constexpr int DP = (kDownqMaxSlots * 16 + 255) / 256;
+  constexpr int AP = kDownqActPieces / kDownqThreads;
+  constexpr int DP = (kDownqMaxSlots * 16 + kDownqThreads - 1) / kDownqThreads;
   u32x4 av[AP], dv[DP];
 #pragma unroll
   for (int k = 0; k < AP; ++k) {
-    const int P = min(tid + 256 * k, nq - 1);
+    const int P = min(tid + kDownqThreads * k, nq - 1);
     const int c = P / pps, within = P % pps;
     const int g = (within % lpr) * CPL + within / lpr;
     av[k] = *reinterpret_cast<const u32x4*>(a.hq + (size_t)s_slot[c] * a.inter + (size_t)g * 16);
   }
 #pragma unroll
   for (int k = 0; k < DP; ++k) {
-    const int P = min(tid + 256 * k, nd - 1);
+    const int P = min(tid + kDownqThreads * k, nd - 1);
     const int c = P / (nb / 4), within = P % (nb / 4);
     dv[k] = *reinterpret_cast<const u32x4*>(a.dh + (size_t)s_slot[c] * nb + (size_t)within * 4);
   }
@@ -781,10 +786,10 @@ __global__ __launch_bounds__(256) void k_downq(DecodeArgs a) {
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int k = 0; k < AP; ++k)
-    if (tid + 256 * k < nq) s_act[tid + 256 * k] = av[k];
+    if (tid + kDownqThreads * k < nq) s_act[tid + kDownqThreads * k] = av[k];
 #pragma unroll
   for (int k = 0; k < DP; ++k)
-    if (tid + 256 * k < nd) s_dh[tid + 256 * k] = dv[k];
+    if (tid + kDownqThreads * k < nd) s_dh[tid + kDownqThreads * k] = dv[k];
   __syncthreads();
   const float* dh = reinterpret_cast<const float*>(s_dh);
   float acc[Q];
@@ -944,8 +949,11 @@ int launch_decode_t(const DecodeArgs& a, int U_max, hipStream_t s) {
         U_max * a.inter <= kDown1ActBytes)
       launch_kernel("down", k_down1<FD>, grid, dim3(256), s, a);
     else if (Q > 1 && a.nb_i == (NBL << a.dn_lpr_log2) && a.nb_i % 4 == 0 && Q * a.K <= kDownqMaxSlots &&
-             Q * a.K * a.inter <= kDownqActPieces * 16)
-      launch_kernel("down", k_downq<FD, Q>, grid, dim3(256), s, a);
+             Q * a.K * a.inter <= kDownqActPieces * 16) {
+      const int rq = (kDownqThreads / 64) * (64 >> a.dn_lpr_log2);   // rows per workgroup
+      QMOE_BOUNDS(rq > 0 && (int64_t)((a.hidden + rq - 1) / rq) * rq >= a.hidden, "decode: down grid covers the rows");
+      launch_kernel("down", k_downq<FD, Q>, dim3((a.hidden + rq - 1) / rq), dim3(kDownqThreads), s, a);
+    }
     else
       launch_kernel("down", k_down<FD, Q>, grid, dim3(256), s, a);
   }
