@@ -81,7 +81,9 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t* __restrict__ W, 
 // lane l is expert 4r + l / 16, token l % 16 of the subtile. The tree is
 // evaluated depth first: its leaves are visited in bit-reversed order and
 // partial sums are kept per level like the digits of a binary counter (level k
-// holds a sum of 2^k leaves). Operands are staged in LDS as fp32, 4 leaves at a
+// holds a sum of 2^k leaves). Two leaves' MFMA chains run interleaved
+// (independent sums; 0.60 -> 0.43 ms for 8192 tokens x 256 experts); four
+// at once measured the same and needed more registers. Operands are staged in LDS as fp32, 4 leaves at a
 // time (the fp16 weights widened exactly once per workgroup), and widened to
 // fp64 at each use: exact, so the products are those of an all-fp64 evaluation.
 typedef double v4d __attribute__((ext_vector_type(4)));
@@ -144,18 +146,10 @@ __global__ __launch_bounds__(256) void k_router_tiles(const uint16_t* __restrict
       }
       __syncthreads();
     }
-#pragma unroll 1
-    for (int k = 0; k < kRtLeaves; ++k) {
-      const int i = i0 + k;   // depth-first leaf index (uniform)
-      v4d acc = {0.0, 0.0, 0.0, 0.0};
-      if (bit_reverse(i, L) < nb) {   // padding leaves are +0
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-          const double a = s_w[k][we + row][4 * st + kg], bx = s_x[k][wt + row][4 * st + kg];
-          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bx, acc, 0, 0, 0);
-        }
-      }
-      // push the leaf: carry through the occupied levels (bits of i), left + right
+    // two leaves at a time: their MFMA chains are independent (each is its own
+    // block's sequential sum), so they are interleaved to keep the matrix unit
+    // busy; the leaves are then pushed in order
+    auto push = [&](int i, const v4d& acc) {   // carry through the occupied levels (bits of i), left + right
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         double carry = acc[c];
@@ -172,6 +166,36 @@ __global__ __launch_bounds__(256) void k_router_tiles(const uint16_t* __restrict
           }
         }
       }
+    };
+#pragma unroll 1
+    for (int k = 0; k < kRtLeaves; k += 2) {
+      const int i = i0 + k;   // depth-first leaf index (uniform)
+      const bool v0 = bit_reverse(i, L) < nb, v1 = bit_reverse(i + 1, L) < nb;   // padding leaves are +0
+      v4d acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+      if (v0 && v1) {
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          const double a0 = s_w[k][we + row][4 * st + kg], b0 = s_x[k][wt + row][4 * st + kg];
+          const double a1 = s_w[k + 1][we + row][4 * st + kg], b1 = s_x[k + 1][wt + row][4 * st + kg];
+          acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc1, 0, 0, 0);
+        }
+      } else {
+        if (v0)
+#pragma unroll
+          for (int st = 0; st < 8; ++st) {
+            const double a0 = s_w[k][we + row][4 * st + kg], b0 = s_x[k][wt + row][4 * st + kg];
+            acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc0, 0, 0, 0);
+          }
+        if (v1)
+#pragma unroll
+          for (int st = 0; st < 8; ++st) {
+            const double a1 = s_w[k + 1][we + row][4 * st + kg], b1 = s_x[k + 1][wt + row][4 * st + kg];
+            acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc1, 0, 0, 0);
+          }
+      }
+      push(i, acc0);
+      push(i + 1, acc1);
     }
   }
   // after P2 = 2^L leaves the whole tree sits at level L
