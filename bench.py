@@ -56,6 +56,7 @@ def parse():
     ap.add_argument("--prefill-only", action="store_true", help="only the 8K-token prefill (for profiling)")
     ap.add_argument("--quantize-only", action="store_true", help="only the weight quantizer (for profiling)")
     ap.add_argument("--decode-q4-only", action="store_true", help="only the q=4 decode (for profiling)")
+    ap.add_argument("--dense-only", action="store_true", help="only the dense FP4 + FP3/H32 mix (for profiling)")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the warm q=1 calls and their kernel times (for the kernel-trace profile)")
     ap.add_argument("--prefill-small-sweep", action="store_true",
@@ -129,6 +130,11 @@ def main():
     if args.quantize_only:
         print(json.dumps({"quantize_fp2": bench_quantize(torch, qm, gen, dev),
                           "quantize_fp3": bench_quantize(torch, qm, gen, dev, fmt=3, rows=4096, k=2048)}), flush=True)
+        return
+    if args.dense_only:
+        res = {}
+        bench_dense(args, torch, qm, gen, dev, res)
+        print(json.dumps(res), flush=True)
         return
     ws = dl.workspace(4)
     if args.decode_q4_only:
@@ -421,9 +427,58 @@ def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
         res["prefill_8k"] = {"status": f"not run: {e}"}
 
     # ---------------------------------------------------------------- dense FP4 + FP3/H32 mix
-    # one qmoe_matvec_group call (two launches: both inputs quantized, then both
-    # matrices' rows), and as the ablation one qmoe_matvec per matrix (three
-    # launches: the 16384-long input is quantized in a launch of its own)
+    fp4, fp3 = bench_dense(args, torch, qm, gen, dev, res)
+
+    # ---------------------------------------------------------------- fused versus expand-then-multiply
+    fp3_big = gen.matvec_case(3, 4096, 16384, ncols=1, seed=0, rot=1)
+    for name, fmt_x, c in (("fp3_4096x2048_h32", 3, fp3), ("fp3_4096x16384_h32", 3, fp3_big),
+                           ("fp4_4096x16384", 4, fp4)):
+        m = qm.device.DeviceMatrix(c)
+        x1 = torch.from_numpy(c.x[:1]).to(dev)
+        y1 = torch.empty((1, c.rows), dtype=torch.float32, device=dev)
+        ws_f = m.workspace(1)
+        ws_x = torch.empty(qm.qmoe_matvec_expanded_workspace_bytes(c.rows, c.k, 1), dtype=torch.uint8, device=dev)
+        t_ = {}
+        for label, fn, w_ in (("fused", qm.qmoe_matvec, ws_f), ("expand_then_multiply", qm.qmoe_matvec_expanded, ws_x)):
+            for _ in range(10):
+                fn(fmt_x, c.rows, c.k, m.w, m.cb, c.rot, x1, y1, w_)
+            with Timer(torch) as tm:
+                for _ in range(K):
+                    fn(fmt_x, c.rows, c.k, m.w, m.cb, c.rot, x1, y1, w_)
+            t_[label] = tm.ms / K * 1e3
+        res[f"matvec_fusion_{name}"] = {"fused_us": round(t_["fused"], 2),
+                                         "expand_then_multiply_us": round(t_["expand_then_multiply"], 2),
+                                         "fused_speedup": round(t_["expand_then_multiply"] / t_["fused"], 2)}
+        log(f"matvec {name} q=1: fused {t_['fused']:.2f} us, expand-then-multiply "
+            f"{t_['expand_then_multiply']:.2f} us ({t_['expand_then_multiply'] / t_['fused']:.2f}x)")
+
+    # ---------------------------------------------------------------- weight quantizer
+    res["quantize_fp2"] = bench_quantize(torch, qm, gen, dev)
+    res["quantize_fp3"] = bench_quantize(torch, qm, gen, dev, fmt=3, rows=4096, k=2048)
+
+    # ---------------------------------------------------------------- FP2 512x256 matvec latency
+    c = gen.fp2_matvec(0)
+    m = qm.device.DeviceMatrix(c)
+    x = torch.from_numpy(c.x).to(dev)
+    y = torch.empty((1, 512), dtype=torch.float32, device=dev)
+    w = m.workspace(1)
+    for _ in range(10):
+        qm.qmoe_matvec(2, 512, 256, m.w, m.cb, 0, x, y, w)
+    with Timer(torch) as t:
+        for _ in range(K):
+            qm.qmoe_matvec(2, 512, 256, m.w, m.cb, 0, x, y, w)
+    res["fp2_matvec_512x256"] = {"us_per_call": round(t.ms / K * 1e3, 2)}
+    return res
+
+
+def bench_dense(args, torch, qm, gen, dev, res):
+    """The dense FP4 4096x16384 + FP3/H32 4096x2048 mix at 1 and 4 columns: one
+    qmoe_matvec_group call (one launch at one column: every workgroup quantizes
+    its matrix's input into LDS; two at four: both inputs quantized, then both
+    matrices' rows), and as the ablation one qmoe_matvec per matrix (three
+    launches: the 16384-long input is quantized in a launch of its own).
+    Returns the last (FP4, FP3) cases."""
+    K = max(20, args.steps // 2)
     for ncols in (1, 4):
         fp4, fp3 = gen.dense_mix(ncols, seed=0)
         mats = [qm.device.DeviceMatrix(c) for c in (fp4, fp3)]
@@ -471,46 +526,7 @@ def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
         log(f"dense mix q={ncols}: {ms * 1e3:.2f} us, {gbs:.1f} GB/s (one qmoe_matvec per matrix: "
             f"{out['per_matrix'] * 1e3:.2f} us); kernels (us): " + ", ".join(f"{k}={v}" for k, v in kern.items()))
 
-    # ---------------------------------------------------------------- fused versus expand-then-multiply
-    fp3_big = gen.matvec_case(3, 4096, 16384, ncols=1, seed=0, rot=1)
-    for name, fmt_x, c in (("fp3_4096x2048_h32", 3, fp3), ("fp3_4096x16384_h32", 3, fp3_big),
-                           ("fp4_4096x16384", 4, fp4)):
-        m = qm.device.DeviceMatrix(c)
-        x1 = torch.from_numpy(c.x[:1]).to(dev)
-        y1 = torch.empty((1, c.rows), dtype=torch.float32, device=dev)
-        ws_f = m.workspace(1)
-        ws_x = torch.empty(qm.qmoe_matvec_expanded_workspace_bytes(c.rows, c.k, 1), dtype=torch.uint8, device=dev)
-        t_ = {}
-        for label, fn, w_ in (("fused", qm.qmoe_matvec, ws_f), ("expand_then_multiply", qm.qmoe_matvec_expanded, ws_x)):
-            for _ in range(10):
-                fn(fmt_x, c.rows, c.k, m.w, m.cb, c.rot, x1, y1, w_)
-            with Timer(torch) as tm:
-                for _ in range(K):
-                    fn(fmt_x, c.rows, c.k, m.w, m.cb, c.rot, x1, y1, w_)
-            t_[label] = tm.ms / K * 1e3
-        res[f"matvec_fusion_{name}"] = {"fused_us": round(t_["fused"], 2),
-                                         "expand_then_multiply_us": round(t_["expand_then_multiply"], 2),
-                                         "fused_speedup": round(t_["expand_then_multiply"] / t_["fused"], 2)}
-        log(f"matvec {name} q=1: fused {t_['fused']:.2f} us, expand-then-multiply "
-            f"{t_['expand_then_multiply']:.2f} us ({t_['expand_then_multiply'] / t_['fused']:.2f}x)")
-
-    # ---------------------------------------------------------------- weight quantizer
-    res["quantize_fp2"] = bench_quantize(torch, qm, gen, dev)
-    res["quantize_fp3"] = bench_quantize(torch, qm, gen, dev, fmt=3, rows=4096, k=2048)
-
-    # ---------------------------------------------------------------- FP2 512x256 matvec latency
-    c = gen.fp2_matvec(0)
-    m = qm.device.DeviceMatrix(c)
-    x = torch.from_numpy(c.x).to(dev)
-    y = torch.empty((1, 512), dtype=torch.float32, device=dev)
-    w = m.workspace(1)
-    for _ in range(10):
-        qm.qmoe_matvec(2, 512, 256, m.w, m.cb, 0, x, y, w)
-    with Timer(torch) as t:
-        for _ in range(K):
-            qm.qmoe_matvec(2, 512, 256, m.w, m.cb, 0, x, y, w)
-    res["fp2_matvec_512x256"] = {"us_per_call": round(t.ms / K * 1e3, 2)}
-    return res
+    return fp4, fp3
 
 
 def bench_probes(torch, qm, dev):
