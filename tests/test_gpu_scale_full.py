@@ -5,6 +5,7 @@ ABI, in the launch configuration the benchmark times.
 The oracle regenerates only the experts that the checked tokens select.
 """
 import concurrent.futures as cf
+import dataclasses
 
 import numpy as np
 import pytest
@@ -14,7 +15,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import bit_block_quantized_rocmfp2_amd as qm  # noqa: E402
-from oracle import dots, moe, router  # noqa: E402
+from oracle import dots, moe, quant, router  # noqa: E402
 from synth import gen  # noqa: E402
 
 TOL = 1e-3
@@ -74,6 +75,55 @@ def test_full_decode_q1(full):
         err = moe.rel_l2(out, ref)
         print(f"q=1 token {t}: experts {idx_ref[0].tolist()} rel_l2 {err:.2e}")
         assert err < TOL
+
+
+@pytest.mark.parametrize("rot_down", [0, 1])
+def test_full_decode_q1_requantized_rows(full, rot_down):
+    """One token at the full shape: the requantized SwiGLU rows and scales in
+    the workspace (all 6 x 64 blocks) equal, bit for bit, column 0 of q = 4 on
+    the same token repeated (a different gate/up kernel), and are within one
+    code of the oracle's; the outputs are equal bit for bit and within the
+    tolerance of the oracle's. rot_down = 1: the same weights with H32 on the
+    down projection's input."""
+    spec, dl, L = full
+    desc = dl.desc
+    if rot_down:
+        desc = qm.make_layer(spec.hidden, spec.inter, spec.n_experts, spec.topk, spec.fmt_gate, spec.fmt_up,
+                             spec.fmt_down, spec.rot_gateup, 1, dl.w_router, None, dl.gate, dl.up, dl.down,
+                             dl.cb_gate, dl.cb_up, dl.cb_down)
+        L = dataclasses.replace(L, rot_down=1)
+    nbi = spec.inter // 32
+    x = gen.tokens(1, spec.hidden, seed=SEED + 6, stream=4)
+
+    def run(xs):
+        xd = qm.device.to_device(xs)
+        out = torch.empty_like(xd)
+        ws = torch.zeros(qm.qmoe_workspace_bytes(desc, xs.shape[0]), dtype=torch.uint8, device="cuda")
+        qm.qmoe_decode_layer(desc, xd, out, ws)
+        torch.cuda.synchronize()
+        lay = qm.qmoe_workspace_layout(desc, xs.shape[0])
+        slots = 4 * spec.topk
+        hq = ws[lay["hq"]: lay["hq"] + slots * spec.inter].cpu().numpy().view(np.int8).reshape(slots, spec.inter)
+        dh = ws[lay["dh"]: lay["dh"] + slots * nbi * 4].cpu().numpy().view(np.float32).reshape(slots, nbi)
+        return out.cpu().numpy(), hq, dh
+
+    o1, hq1, dh1 = run(x)
+    o4, hq4, dh4 = run(np.repeat(x, 4, axis=0))
+    assert np.array_equal(o1[0], o4[0])
+    rows = [4 * u for u in range(spec.topk)]
+    assert np.array_equal(hq1[rows], hq4[rows]) and np.array_equal(dh1[rows], dh4[rows])
+    idx_ref, _, _ = router.route(dl.w_router_host, x, None, spec.topk)
+    xq, dx = quant.quantize_act(x[0], spec.rot_gateup)
+    diffs = 0
+    for u, e in enumerate(idx_ref[0]):
+        _, _, hq_ref, dh_ref = moe.expert_ffn(L, int(e), xq, dx)
+        d = np.abs(hq1[4 * u].astype(int) - hq_ref.astype(int))
+        assert d.max() <= 1
+        diffs += int(np.sum(d != 0))
+        assert np.allclose(dh1[4 * u], dh_ref, rtol=1e-5, atol=0)
+    assert diffs <= 0.01 * spec.inter * spec.topk
+    ref, _, _ = moe.moe_tokens(L, x)
+    assert moe.rel_l2(o1, ref) < TOL
 
 
 def test_full_decode_q1_top4(full):
