@@ -375,6 +375,30 @@ def bench_extra(args, torch, qm, gen, spec, dl, ws, per_expert, dev):
                                    "packed_bytes_read": 4 * spec.topk * per_expert}
     log(f"decode q=4 as four q=1 calls: {ms_pc * 1e3:.2f} us ({ms_pc / ms:.2f}x the decode-once call)")
 
+    # ablation: the same groups with the expert products on the int8 matrix
+    # cores (qmoe_decode_layer_mfma: the 4 tokens as the MFMA's 4 columns)
+    for i in range(10):
+        qm.qmoe_decode_layer_mfma(dl.desc, groups[i % len(groups)], out, ws)
+    with Timer(torch) as t_mx:
+        for i in range(K):
+            qm.qmoe_decode_layer_mfma(dl.desc, groups[i % len(groups)], out, ws)
+    ms_mx = t_mx.ms / K
+    qm.qmoe_timing_enable(True)
+    for i in range(K):
+        qm.qmoe_decode_layer_mfma(dl.desc, groups[i % len(groups)], out, ws)
+    torch.cuda.synchronize()
+    kern_mx = {}
+    for name in ("route", "gateup_mx", "down_mx"):
+        avg, _ = kernel_avg_ms(qm, name)
+        if avg:
+            kern_mx[name] = round(avg * 1e3, 2)
+    qm.qmoe_timing_enable(False)
+    res["decode_q4_mfma"] = {"us_per_call": round(ms_mx * 1e3, 2), "tokens_per_s": round(4 / (ms_mx * 1e-3), 1),
+                             "vs_dot4_call": round(ms_mx / ms, 3), "kernel_us": kern_mx,
+                             "entry_point": "qmoe_decode_layer_mfma"}
+    log(f"decode q=4 with the products on v_mfma_i32_4x4x4_16b_i8: {ms_mx * 1e3:.2f} us ({ms_mx / ms:.2f}x the "
+        f"dot4 call); kernels (us): " + ", ".join(f"{k}={v}" for k, v in kern_mx.items()))
+
     # routing variant: the same layer with top-4 routing, q = 1
     desc4 = qm.make_layer(spec.hidden, spec.inter, spec.n_experts, 4, spec.fmt_gate, spec.fmt_up, spec.fmt_down,
                           spec.rot_gateup, spec.rot_down, dl.w_router, None, dl.gate, dl.up, dl.down, dl.cb_gate,

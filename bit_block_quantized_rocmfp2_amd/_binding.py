@@ -84,6 +84,8 @@ def load_library(path=None):
                                c_void_p]),
         "qmoe_decode_layer": (c_int, [POINTER(qmoe_layer), c_void_p, c_int32, c_void_p, c_void_p, c_size_t,
                                       c_void_p]),
+        "qmoe_decode_layer_mfma": (c_int, [POINTER(qmoe_layer), c_void_p, c_int32, c_void_p, c_void_p, c_size_t,
+                                           c_void_p]),
         "qmoe_decode_noalloc_max_bytes": (c_size_t, []),
         "qmoe_decode_layer_noalloc": (c_int, [POINTER(qmoe_layer), c_void_p, c_int32, c_void_p, c_void_p]),
         "qmoe_prefill_layer": (c_int, [POINTER(qmoe_layer), c_void_p, c_int32, c_void_p, c_void_p, c_size_t,
@@ -124,7 +126,7 @@ LIB = load_library()
 EXPORTED = (
     "qmoe_strerror", "qmoe_last_error", "qmoe_version", "qmoe_block_bytes", "qmoe_packed_bytes", "qmoe_pack",
     "qmoe_unpack", "qmoe_layer_check", "qmoe_workspace_bytes", "qmoe_workspace_layout", "qmoe_route",
-    "qmoe_decode_layer", "qmoe_decode_noalloc_max_bytes", "qmoe_decode_layer_noalloc", "qmoe_prefill_layer", "qmoe_prefill_layer_ex",
+    "qmoe_decode_layer", "qmoe_decode_layer_mfma", "qmoe_decode_noalloc_max_bytes", "qmoe_decode_layer_noalloc", "qmoe_prefill_layer", "qmoe_prefill_layer_ex",
     "qmoe_matvec_workspace_bytes", "qmoe_matvec_group_workspace_bytes", "qmoe_matvec_group", "qmoe_matvec", "qmoe_quant_act",
     "qmoe_block_dots", "qmoe_block_dots_mfma", "qmoe_matvec_expanded_workspace_bytes", "qmoe_matvec_expanded",
     "qmoe_quantize_workspace_bytes", "qmoe_quantize", "qmoe_timing_enable", "qmoe_timing_read", "qmoe_probe_read",
@@ -238,6 +240,11 @@ def qmoe_route(L, x, idx, gate_w, ws, stream=None) -> None:
 def qmoe_decode_layer(L, x, out, ws, stream=None) -> None:
     _check(LIB.qmoe_decode_layer(ctypes.byref(L), _ptr(x), x.shape[0], _ptr(out), _ptr(ws), _nbytes(ws),
                                  _stream(stream)), "qmoe_decode_layer")
+
+
+def qmoe_decode_layer_mfma(L, x, out, ws, stream=None) -> None:
+    _check(LIB.qmoe_decode_layer_mfma(ctypes.byref(L), _ptr(x), x.shape[0], _ptr(out), _ptr(ws), _nbytes(ws),
+                                      _stream(stream)), "qmoe_decode_layer_mfma")
 
 
 def qmoe_decode_layer_noalloc(L, x, out, stream=None) -> None:

@@ -140,9 +140,9 @@ struct PlanLds {
   int ids[4][8];          // plan writer only: selected ids of token t, ascending
   float w[4][8];          // plan writer only: their routing weights
   int e;                  // one token: the expert of this workgroup's plan slot
-  int uid[kPlanMax];      // q > 1: plan slot s -> its expert (the s-th distinct id, ascending)
-  uint32_t umask[kPlanMax];  // q > 1: its column mask
-  int U;                  // q > 1: plan size
+  int uid[kPlanMax];      // plan slot s -> its expert (the s-th distinct id, ascending)
+  uint32_t umask[kPlanMax];  // its column mask
+  int U;                  // plan size
 };
 
 // Workgroup barrier that orders LDS accesses only: this wave's LDS operations
@@ -156,7 +156,8 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Every workgroup selects the experts itself. With one token wave 0 runs the
 // top-k and passes the expert of slot u (the plan is the K ids ascending with
-// column mask 1) to the other waves through LDS. With q > 1 tokens, waves t < q
+// column mask 1) to the other waves through LDS, and lists the plan in P.uid,
+// P.umask, P.U. With q > 1 tokens, waves t < q
 // select token t and set its experts in an LDS bitmap; after one barrier wave 0
 // lists the union of the bitmaps in LDS: plan slot s holds the s-th set bit,
 // i.e. the distinct ids in ascending order, and its column mask is that bit
@@ -175,7 +176,14 @@ __device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, in
     if (wave == 0) {
       const uint64_t first = topk_select(a.logits, a.E, a.K, lane, p);
       const int eu = (u < a.K) ? __builtin_amdgcn_readlane(p.id, topk_lane_of_rank(p, u)) : -1;
-      if (lane == 0) P.e = eu;
+      if (lane == 0) {
+        P.e = eu;
+        P.U = a.K;
+      }
+      if (lane < a.K) {   // the plan list (slot = rank in ascending id), as for q > 1
+        P.uid[p.rank] = p.id;
+        P.umask[p.rank] = 1u;
+      }
       if (write) {
         const float g = topk_softmax(p, first, a.K, lane);
         if (lane < a.K) {
@@ -362,17 +370,13 @@ __device__ __forceinline__ void gateup_wave_swiglu(uint32_t mask, const float (&
   }
 }
 
-// SwiGLU of the workgroup's 32 rows (wave w holds rows RPW*w .. RPW*w + RPW-1 as
-// per-lane partial sums) and requantization of the 32-row block (+ H32) for each
-// routed column of slot u.
-template <int Q, int RPW>
-__device__ __forceinline__ void gateup_epilogue(const DecodeArgs& a, uint32_t mask, int u, int rb,
-                                                const float (&ag)[RPW][Q], const float (&au)[RPW][Q],
-                                                float (&s_a)[4][32]) {
+// Requantization (+ H32) of the 32 SwiGLU values s_a[t][0..31] of each routed
+// column t of slot u, row block rb, into hq / dh: half-wave h of wave w takes
+// column 2w + h.
+template <int Q>
+__device__ __forceinline__ void requant_item(const DecodeArgs& a, uint32_t mask, int u, int rb,
+                                             const float (&s_a)[4][32]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  gateup_wave_swiglu<Q, RPW>(mask, ag, au, s_a, wave * RPW);
-  __syncthreads();
-  // requantize the 32-row block: half-wave h of wave w takes column 2w + h
   if (wave < (Q + 1) / 2) {
     const int t = 2 * wave + (lane >> 5), j = lane & 31;
     const bool act = t < Q && (mask >> t & 1);
@@ -384,6 +388,19 @@ __device__ __forceinline__ void gateup_epilogue(const DecodeArgs& a, uint32_t ma
       if (j == 0) a.dh[slot * a.nb_i + rb] = d;
     }
   }
+}
+
+// SwiGLU of the workgroup's 32 rows (wave w holds rows RPW*w .. RPW*w + RPW-1 as
+// per-lane partial sums) and requantization of the 32-row block (+ H32) for each
+// routed column of slot u.
+template <int Q, int RPW>
+__device__ __forceinline__ void gateup_epilogue(const DecodeArgs& a, uint32_t mask, int u, int rb,
+                                                const float (&ag)[RPW][Q], const float (&au)[RPW][Q],
+                                                float (&s_a)[4][32]) {
+  const int wave = threadIdx.x >> 6;
+  gateup_wave_swiglu<Q, RPW>(mask, ag, au, s_a, wave * RPW);
+  __syncthreads();
+  requant_item<Q>(a, mask, u, rb, s_a);
 }
 
 // The gate and up rows row0 .. row0+RPW-1 of expert e against the routed
@@ -973,6 +990,316 @@ int launch_decode_q(const DecodeArgs& a, int U_max, int fg, int fd, hipStream_t 
   return launch_decode_t<4, 4, Q>(a, U_max, s);
 }
 
+// ------------------------------------------------------------ decode on the matrix cores
+// The same layer with the expert products on v_mfma_i32_4x4x4_16b_i8, which
+// computes 16 independent 4 x 4 x 4 int8 products per instruction. Its 4 rows
+// are 4 weight rows (2 gate + 2 up rows, or 4 down rows), its 4 columns the
+// q <= 4 tokens (a column is zero past q and for a token not routed to the
+// expert), and its 16 blocks 16 consecutive 32-weight blocks of those rows;
+// 8 instructions (K = 4 each) give the exact int32 sum of every (row, token,
+// block). Lane l = 4b + i supplies row i's weights of block b (expanded by byte
+// permutes as for sdot4) and token i's activations of block b, and receives
+// the sums of rows 0..3 of block b for token i. It adds float(P) * (s_w * d_x)
+// per row in block order, and the 16 lanes of each token are then summed by
+// xor butterflies over lane bits 2..5. That order is its own (results within
+// the oracle's tolerance, not the bits of qmoe_decode_layer) and the same for
+// every q, so column t of q tokens equals a one-token call bit for bit.
+// ([Strix-284B] decode section: each block decoded once for the q = 4
+// verification columns; here the q columns are the MFMA's N dimension.)
+typedef int v4i __attribute__((ext_vector_type(4)));
+constexpr int kMxMaxNbH = 256;    // gate/up rows of at most 8192 weights
+constexpr int kMxGroups = 8;      // 16-block groups per pass of a gate/up row
+constexpr int kMxMaxNbI = 64;     // down rows of at most 2048 weights: one group per wave
+constexpr int kMxUB = 12;         // down: experts whose weights are requested together
+constexpr int kDownmActBytes = 64 * 1024;
+
+// Exact int32 sums of one block for the lane's row and token (see above).
+__device__ __forceinline__ v4i mfma4_block(const uint32_t w[8], const uint32_t x[8]) {
+  v4i c = {0, 0, 0, 0};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) c = __builtin_amdgcn_mfma_i32_4x4x4i8((int)w[k], (int)x[k], c, 0, 0, 0);
+  return c;
+}
+
+// acc[r] += float(P[r]) * (s_w(row r) * f) for the 4 rows of the lane's block:
+// the scales of rows 0..3 come from lanes 4b + 0..3 of the quad (DPP broadcasts).
+__device__ __forceinline__ void mfma4_accumulate(const v4i& P, float sw, float f, float (&acc)[4]) {
+  const float s0 = dpp_f32<0x00>(sw), s1 = dpp_f32<0x55>(sw), s2 = dpp_f32<0xAA>(sw), s3 = dpp_f32<0xFF>(sw);
+  acc[0] = fmaf((float)P[0], s0 * f, acc[0]);
+  acc[1] = fmaf((float)P[1], s1 * f, acc[1]);
+  acc[2] = fmaf((float)P[2], s2 * f, acc[2]);
+  acc[3] = fmaf((float)P[3], s3 * f, acc[3]);
+}
+
+// Sum over the 16 lanes that share lane & 3 (all 64 lanes active).
+__device__ __forceinline__ float sum_lane_bits2to5(float v) {
+  v = v + xchg32<4>(v);
+  v = v + xchg32<8>(v);
+  v = v + xchg32<16>(v);
+  return v + __shfl_xor(v, 32);
+}
+
+// Gate/up: one workgroup of 16 waves per CU walks the (slot, 32-row) items as
+// k_gateupq2 does; wave w takes gate rows 2w, 2w + 1 and up rows 2w, 2w + 1 of
+// the item as MFMA rows 0..3. The tokens' int8 rows and scales are copied to
+// LDS once (by the waves that do not select, during the selection), each row
+// padded by one 16-byte piece so that the 4 tokens of a read fall in distinct
+// banks.
+template <int FMT, int Q>
+__global__ __launch_bounds__(1024) void k_gateupm(DecodeArgs a) {
+  constexpr int XT = 2 * kMxMaxNbH + 1;   // 16-byte pieces per token row in LDS
+  constexpr int DT = kMxMaxNbH + 1;
+  __shared__ float s_a[4][32];
+  __shared__ PlanLds P;
+  __shared__ u32x4 s_xq[Q * XT];
+  __shared__ float s_dx[Q * DT];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nb = a.nb_h;
+  constexpr int NCP = 1024 - 64 * Q;                              // copying threads
+  constexpr int NXP = (Q * 2 * kMxMaxNbH + NCP - 1) / NCP;        // 16-byte pieces per copying thread
+  constexpr int NDP = (Q * kMxMaxNbH + NCP - 1) / NCP;            // scales per copying thread
+  const int ct = tid - 64 * Q;
+  const int npx = Q * nb * 2, npd = Q * nb;
+  u32x4 xv[NXP];
+  float dv[NDP];
+  if (ct >= 0) {   // (uniform per wave)
+#pragma unroll
+    for (int k = 0; k < NXP; ++k) xv[k] = reinterpret_cast<const u32x4*>(a.xq)[min(ct + NCP * k, npx - 1)];
+#pragma unroll
+    for (int k = 0; k < NDP; ++k) dv[k] = a.dx[min(ct + NCP * k, npd - 1)];
+  }
+  uint32_t mask0;
+  int U;
+  topk_and_plan<Q>(a, P, 0, blockIdx.x == 0, mask0, &U);
+  if (ct >= 0) {
+#pragma unroll
+    for (int k = 0; k < NXP; ++k) {
+      const int i = ct + NCP * k;
+      if (i < npx) s_xq[(i / (nb * 2)) * XT + i % (nb * 2)] = xv[k];
+    }
+#pragma unroll
+    for (int k = 0; k < NDP; ++k) {
+      const int i = ct + NCP * k;
+      if (i < npd) s_dx[(i / nb) * DT + i % nb] = dv[k];
+    }
+  }
+  __syncthreads();
+  const int i4 = lane & 3, b = lane >> 2;
+  const int tq = min(i4, Q - 1);   // the lane's token column (read in range; zeroed when not live)
+  const int nrb = a.inter / 32;
+  const int G = nb >> 4;
+  const bool is_up = i4 >= 2;
+  for (int it = blockIdx.x; it < U * nrb; it += gridDim.x) {
+    const int u = it / nrb, rb = it % nrb;
+    const uint32_t mask = P.umask[u];
+    const int e = min(max(P.uid[u], 0), a.E - 1);   // (a plan id is in range; the clamp keeps any address so)
+    const bool live = i4 < Q && ((mask >> i4) & 1u);
+    const int row = rb * 32 + 2 * wave + (i4 & 1);
+    const uint8_t* rp = (is_up ? a.up : a.gate) + (size_t)e * a.gu_stride + (size_t)row * a.gu_row_bytes;
+    uint32_t cb[4];
+    load_codebook<FMT>((is_up ? a.cb_up : a.cb_gate) + ((size_t)e << FMT), cb);
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int g0 = 0; g0 < G; g0 += kMxGroups) {
+      // every block load of the pass is requested (index clamped) before any is used
+      Blocks<FMT, 1> bl[kMxGroups];
+#pragma unroll
+      for (int k = 0; k < kMxGroups; ++k) bl[k].load(rp, nb, min(16 * (g0 + k) + b, nb - 1));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < kMxGroups; ++k)
+        if (g0 + k < G) {   // uniform
+          const int blk = 16 * (g0 + k) + b;
+          uint32_t w[8];
+          bl[k].expand(0, cb, w);
+          const u32x4 x0 = s_xq[tq * XT + 2 * blk], x1 = s_xq[tq * XT + 2 * blk + 1];
+          const uint32_t xr[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          uint32_t xw[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xw[j] = live ? xr[j] : 0u;
+          mfma4_accumulate(mfma4_block(w, xw), bl[k].scale(0), s_dx[tq * DT + blk], acc);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = sum_lane_bits2to5(acc[r]);
+    // lane t < Q holds the gate (acc[0], acc[1]) and up (acc[2], acc[3]) sums of
+    // rows 2w, 2w + 1 for token t
+    if (lane < Q && ((mask >> lane) & 1u)) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) s_a[lane][2 * wave + r] = acc[r] / (1.0f + expf(-acc[r])) * acc[2 + r];
+    }
+    __syncthreads();
+    requant_item<Q>(a, mask, u, rb, s_a);
+    __syncthreads();   // s_a is reused by the next item
+  }
+}
+
+// Down: one workgroup of 16 waves per 16 rows: wave w takes rows 4 (w % 4) ..
+// + 3 as MFMA rows and the blocks of K quarter w / 4 (one 16-block group for
+// inter 2048), for every planned expert in ascending id; the four quarters'
+// sums meet in LDS in quarter order. The routed slots' activations are copied
+// to LDS once per workgroup, each slot row padded by one 16-byte piece.
+template <int FMT, int Q>
+__global__ __launch_bounds__(1024) void k_downm(DecodeArgs a) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int rq = wave & 3, kq = wave >> 2;
+  const int nb = a.nb_i;
+  const int SS = 2 * nb + 1;   // 16-byte pieces per slot row in LDS
+  constexpr int DS = kMxMaxNbI + 1;
+  __shared__ int s_plan[kPlanWOff + 4 * kPlanMax];
+  __shared__ int s_slot[kDownqMaxSlots];
+  __shared__ int s_cidx[4 * kPlanMax];
+  __shared__ int s_nslot;
+  __shared__ u32x4 s_act[kDownmActBytes / 16];
+  __shared__ float s_dh[kDownqMaxSlots * DS];
+  __shared__ float s_part[4][4][4][4];   // [K quarter][row quad][token][row]
+  static_assert(kPlanWOff + 4 * kPlanMax == 256, "plan fits one load per thread of the first 256");
+  if (tid < 256) s_plan[tid] = a.plan[tid];
+  __syncthreads();
+  const int U = s_plan[0];
+  const float* pw = reinterpret_cast<const float*>(s_plan + kPlanWOff);
+  if (wave == 0) {
+    // lane u < U: its routed columns; compact slots by ballots (as k_downq)
+    const uint32_t m = (lane < U) ? ((uint32_t)s_plan[kPlanMaskOff + lane] & ((1u << Q) - 1u)) : 0u;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int base = 0, total = 0;
+#pragma unroll
+    for (int t = 0; t < Q; ++t) {
+      const uint64_t bt = __ballot((m >> t) & 1u);
+      base += __popcll(bt & lt);
+      total += __popcll(bt);
+    }
+    int c = base;
+#pragma unroll
+    for (int t = 0; t < Q; ++t)
+      if ((m >> t) & 1u) {
+        s_slot[c] = lane * 4 + t;
+        s_cidx[lane * 4 + t] = c;
+        ++c;
+      }
+    if (lane == 0) s_nslot = total;
+  }
+  __syncthreads();
+  const int nslot = s_nslot;
+  // activations of the listed slots into registers (indices clamped), then the
+  // first experts' weights, then the LDS stores
+  constexpr int AP = kDownmActBytes / 16 / 1024;
+  const int pps = nb * 2, nq = nslot * pps, nd = nslot * (nb / 4);
+  u32x4 av[AP], dv;
+#pragma unroll
+  for (int k = 0; k < AP; ++k) {
+    const int i = min(tid + 1024 * k, nq - 1);
+    av[k] = *reinterpret_cast<const u32x4*>(a.hq + (size_t)s_slot[i / pps] * a.inter + (size_t)(i % pps) * 16);
+  }
+  {
+    const int i = min(tid, nd - 1);
+    dv = *reinterpret_cast<const u32x4*>(a.dh + (size_t)s_slot[i / (nb / 4)] * nb + (size_t)(i % (nb / 4)) * 4);
+  }
+  const int i4 = lane & 3, b = lane >> 2;
+  const int row = blockIdx.x * 16 + 4 * rq + i4;           // the lane's weight row
+  const int rowc = min(row, a.hidden - 1);
+  const bool has_group = 16 * kq < nb;                      // (uniform) this quarter holds a group
+  const int blk = min(16 * kq + b, nb - 1);
+  int ej[kMxUB];
+  uint32_t cb[kMxUB][4];
+  Blocks<FMT, 1> bl[kMxUB];
+#pragma unroll
+  for (int j = 0; j < kMxUB; ++j) {
+    ej[j] = (j < U) ? min(max(s_plan[kPlanIdOff + j], 0), a.E - 1) : 0;
+    load_codebook<FMT>(a.cb_down + ((size_t)ej[j] << FMT), cb[j]);
+    bl[j].load(a.down + (size_t)ej[j] * a.dn_stride + (size_t)rowc * a.dn_row_bytes, nb, blk);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < AP; ++k) {
+    const int i = tid + 1024 * k;
+    if (i < nq) s_act[(i / pps) * SS + i % pps] = av[k];
+  }
+  if (tid < nd) {
+    const int c = tid / (nb / 4), o = (tid % (nb / 4)) * 4;
+    s_dh[c * DS + o] = __uint_as_float(dv.x);
+    s_dh[c * DS + o + 1] = __uint_as_float(dv.y);
+    s_dh[c * DS + o + 2] = __uint_as_float(dv.z);
+    s_dh[c * DS + o + 3] = __uint_as_float(dv.w);
+  }
+  __syncthreads();
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int u0 = 0; u0 < U; u0 += kMxUB) {
+    if (u0 > 0) {   // further experts (more than kMxUB planned)
+#pragma unroll
+      for (int j = 0; j < kMxUB; ++j) {
+        ej[j] = (u0 + j < U) ? min(max(s_plan[kPlanIdOff + u0 + j], 0), a.E - 1) : 0;
+        load_codebook<FMT>(a.cb_down + ((size_t)ej[j] << FMT), cb[j]);
+        bl[j].load(a.down + (size_t)ej[j] * a.dn_stride + (size_t)rowc * a.dn_row_bytes, nb, blk);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMxUB; ++j) {
+      const int u = u0 + j;
+      if (has_group && u < U) {   // uniform
+        const uint32_t mask = (uint32_t)s_plan[kPlanMaskOff + u];
+        const bool live = i4 < Q && ((mask >> i4) & 1u);
+        const int c = live ? s_cidx[u * 4 + i4] : 0;
+        uint32_t w[8];
+        bl[j].expand(0, cb[j], w);
+        const u32x4 x0 = s_act[c * SS + 2 * blk], x1 = s_act[c * SS + 2 * blk + 1];
+        const uint32_t xr[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        uint32_t xw[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) xw[k] = live ? xr[k] : 0u;
+        const float wgt = live ? pw[4 * u + i4] : 0.0f;
+        const v4i P4 = mfma4_block(w, xw);
+        // (s_w * d_h) * routing weight, as k_downq
+        const float sw = bl[j].scale(0), dht = s_dh[c * DS + blk];
+        const float s0 = dpp_f32<0x00>(sw), s1 = dpp_f32<0x55>(sw), s2 = dpp_f32<0xAA>(sw), s3 = dpp_f32<0xFF>(sw);
+        acc[0] = fmaf((float)P4[0], s0 * dht * wgt, acc[0]);
+        acc[1] = fmaf((float)P4[1], s1 * dht * wgt, acc[1]);
+        acc[2] = fmaf((float)P4[2], s2 * dht * wgt, acc[2]);
+        acc[3] = fmaf((float)P4[3], s3 * dht * wgt, acc[3]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] = sum_lane_bits2to5(acc[r]);
+  if (lane < 4) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_part[kq][rq][lane][r] = acc[r];
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int q4 = tid >> 4, t = (tid >> 2) & 3, r = tid & 3;
+    const float v = ((s_part[0][q4][t][r] + s_part[1][q4][t][r]) + s_part[2][q4][t][r]) + s_part[3][q4][t][r];
+    const int orow = blockIdx.x * 16 + 4 * q4 + r;
+    if (t < Q && orow < a.hidden) a.out[(size_t)t * a.hidden + orow] = v;
+  }
+}
+
+template <int FG, int FD, int Q>
+int launch_decode_mfma_t(const DecodeArgs& a, hipStream_t s) {
+  {
+    const int nq = (a.q * a.nb_h + a.quant_per_wg - 1) / a.quant_per_wg;
+    launch_kernel("route", k_route<Q>, dim3(a.E + nq), dim3(128 * Q), s, a);
+  }
+  int st = launch_check("route");
+  if (st) return st;
+  launch_kernel("gateup_mx", k_gateupm<FG, Q>, dim3(device_cu_count()), dim3(1024), s, a);
+  if ((st = launch_check("gateup_mx"))) return st;
+  launch_kernel("down_mx", k_downm<FD, Q>, dim3((a.hidden + 15) / 16), dim3(1024), s, a);
+  return launch_check("down_mx");
+}
+
+template <int Q>
+int launch_decode_mfma_q(const DecodeArgs& a, int fg, int fd, hipStream_t s) {
+  if (fg == 2 && fd == 3) return launch_decode_mfma_t<2, 3, Q>(a, s);
+  if (fg == 2 && fd == 2) return launch_decode_mfma_t<2, 2, Q>(a, s);
+  if (fg == 2 && fd == 4) return launch_decode_mfma_t<2, 4, Q>(a, s);
+  if (fg == 3 && fd == 3) return launch_decode_mfma_t<3, 3, Q>(a, s);
+  if (fg == 3 && fd == 2) return launch_decode_mfma_t<3, 2, Q>(a, s);
+  if (fg == 3 && fd == 4) return launch_decode_mfma_t<3, 4, Q>(a, s);
+  if (fg == 4 && fd == 3) return launch_decode_mfma_t<4, 3, Q>(a, s);
+  if (fg == 4 && fd == 2) return launch_decode_mfma_t<4, 2, Q>(a, s);
+  return launch_decode_mfma_t<4, 4, Q>(a, s);
+}
+
 // ------------------------------------------------------------ prefill: experts with few pairs
 // Experts that 1 .. kPrefillSmallPairs pairs of a prefill batch route to would
 // fill an MFMA tile with padding; their pairs take the q <= 4 matvec arithmetic
@@ -1145,9 +1472,11 @@ int launch_prefill_small(const PrefillSmall& p, hipStream_t s) {
 
 }  // namespace qmoe
 
-extern "C" int qmoe_decode_layer(const qmoe_layer* L, const float* x, int32_t q, float* out, void* ws,
-                                 size_t ws_bytes, void* stream) {
-  clear_error();
+namespace {
+
+// Checks the arguments of a decode call and fills the kernels' argument block.
+int decode_setup(const qmoe_layer* L, const float* x, int32_t q, float* out, void* ws, size_t ws_bytes,
+                 DecodeArgs& a, int& U_max) {
   if (q < 1 || q > 4) QMOE_FAIL(QMOE_E_SHAPE, "q=%d outside 1..4", q);
   WsPtrs w;
   int st = ws_ptrs(L, q, ws, ws_bytes, &w);
@@ -1157,7 +1486,7 @@ extern "C" int qmoe_decode_layer(const qmoe_layer* L, const float* x, int32_t q,
   FormatInfo fg, fd;
   format_info(L->fmt_gate, &fg);
   format_info(L->fmt_down, &fd);
-  DecodeArgs a{};
+  a = DecodeArgs{};
   a.w_router = L->w_router;
   a.bias = L->router_bias;
   a.gate = static_cast<const uint8_t*>(L->gate);
@@ -1191,7 +1520,7 @@ extern "C" int qmoe_decode_layer(const qmoe_layer* L, const float* x, int32_t q,
   a.dn_stride = a.dn_row_bytes * L->hidden;
   a.dn_lpr_log2 = ilog2(lanes_per_row(a.nb_i, L->fmt_down == QMOE_FP4 ? 1 : 2));
   a.quant_per_wg = 4 * q;   // blocks per token-quantization workgroup: one pass of its half-waves
-  const int U_max = std::min(q * L->topk, L->n_experts);
+  U_max = std::min(q * L->topk, L->n_experts);
   {   // the extents the decode kernels address (slot = 4 u + t for plan slot u, column t)
     const size_t maxslot = (size_t)(U_max - 1) * 4 + (q - 1);
     QMOE_BOUNDS((size_t)q * a.hidden <= w.n_xq && (size_t)q * a.nb_h * 4 <= w.n_dx, "decode: quantized tokens");
@@ -1202,11 +1531,50 @@ extern "C" int qmoe_decode_layer(const qmoe_layer* L, const float* x, int32_t q,
                 "decode: requantized intermediate rows");
     QMOE_BOUNDS(a.inter % 32 == 0 && 4 * (64 >> a.dn_lpr_log2) > 0, "decode: gate/up row blocks, down rows per group");
   }
+  return QMOE_OK;
+}
+
+}  // namespace
+
+extern "C" int qmoe_decode_layer(const qmoe_layer* L, const float* x, int32_t q, float* out, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  clear_error();
+  DecodeArgs a;
+  int U_max = 0;
+  int st = decode_setup(L, x, q, out, ws, ws_bytes, a, U_max);
+  if (st) return st;
   hipStream_t s = as_stream(stream);
   switch (q) {
     case 1: return launch_decode_q<1>(a, U_max, L->fmt_gate, L->fmt_down, s);
     case 2: return launch_decode_q<2>(a, U_max, L->fmt_gate, L->fmt_down, s);
     case 3: return launch_decode_q<3>(a, U_max, L->fmt_gate, L->fmt_down, s);
     default: return launch_decode_q<4>(a, U_max, L->fmt_gate, L->fmt_down, s);
+  }
+}
+
+extern "C" int qmoe_decode_layer_mfma(const qmoe_layer* L, const float* x, int32_t q, float* out, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  clear_error();
+  DecodeArgs a;
+  int U_max = 0;
+  int st = decode_setup(L, x, q, out, ws, ws_bytes, a, U_max);
+  if (st) return st;
+  if (a.nb_h % 16 != 0 || a.nb_h > kMxMaxNbH)
+    QMOE_FAIL(QMOE_E_SHAPE, "matrix-core decode: hidden=%d must be a multiple of 512 and at most %d", a.hidden,
+              32 * kMxMaxNbH);
+  if (a.nb_i % 16 != 0 || a.nb_i > kMxMaxNbI)
+    QMOE_FAIL(QMOE_E_SHAPE, "matrix-core decode: inter=%d must be a multiple of 512 and at most %d", a.inter,
+              32 * kMxMaxNbI);
+  if (q * a.K > kDownqMaxSlots || (int64_t)q * a.K * (2 * a.nb_i + 1) * 16 > kDownmActBytes)
+    QMOE_FAIL(QMOE_E_SHAPE, "matrix-core decode: q * topk = %d routed slots of %d blocks exceed the down "
+              "kernel's LDS", q * a.K, a.nb_i);
+  QMOE_BOUNDS((int64_t)((a.hidden + 15) / 16) * 16 >= a.hidden && a.inter % 32 == 0,
+              "matrix-core decode: down grid covers the rows, gate/up items of 32 rows");
+  hipStream_t s = as_stream(stream);
+  switch (q) {
+    case 1: return launch_decode_mfma_q<1>(a, L->fmt_gate, L->fmt_down, s);
+    case 2: return launch_decode_mfma_q<2>(a, L->fmt_gate, L->fmt_down, s);
+    case 3: return launch_decode_mfma_q<3>(a, L->fmt_gate, L->fmt_down, s);
+    default: return launch_decode_mfma_q<4>(a, L->fmt_gate, L->fmt_down, s);
   }
 }

@@ -155,6 +155,22 @@ int qmoe_route(const qmoe_layer* L, const float* x, int32_t ntok, int32_t* idx,
 int qmoe_decode_layer(const qmoe_layer* L, const float* x, int32_t q, float* out,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* The same decode with the expert products on the int8 matrix cores
+ * (v_mfma_i32_4x4x4_16b_i8: the q <= 4 tokens are the instruction's 4
+ * columns, 4 weight rows its rows, 16 consecutive 32-weight blocks its 16
+ * blocks), each packed block still read and expanded once for all q columns
+ * ([Strix-284B] decode section; the routed experts' products with q padded to
+ * the matrix core's width). Per-block int32 sums are exact as on the dot4 path;
+ * the fp32 accumulation runs in an order of its own, so results agree with
+ * qmoe_decode_layer within the layer tolerance, not bit for bit, and column t
+ * of a q-token call equals a one-token call of this function bit for bit.
+ * Arguments, workspace and errors as qmoe_decode_layer; in addition hidden and
+ * inter must be multiples of 512 with hidden <= 8192 and inter <= 2048, and
+ * q * topk routed slots of inter/32 blocks must fit the down kernel's 64 KB of
+ * staged activations, else QMOE_E_SHAPE before any launch. */
+int qmoe_decode_layer_mfma(const qmoe_layer* L, const float* x, int32_t q, float* out,
+                           void* ws, size_t ws_bytes, void* stream);
+
 /* Decode for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc. The same
  * computation and kernels as qmoe_decode_layer, but the workspace is a fixed

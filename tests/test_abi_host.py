@@ -211,6 +211,10 @@ def test_launch_entry_points_reject_before_launch():
     assert st == -6
     st = B.LIB.qmoe_decode_layer(ctypes.byref(L), x.ctypes.data, 1, out.ctypes.data, None, 0, None)
     assert st == -6
+    st = B.LIB.qmoe_decode_layer_mfma(ctypes.byref(L), x.ctypes.data, 5, out.ctypes.data, ws.ctypes.data, 16, None)
+    assert st == -2
+    st = B.LIB.qmoe_decode_layer_mfma(ctypes.byref(L), x.ctypes.data, 1, out.ctypes.data, ws.ctypes.data, 16, None)
+    assert st == -6
     st = B.LIB.qmoe_quant_act(x.ctypes.data, 4, 256, 2, out.ctypes.data, out.ctypes.data, None)
     assert st == -3
     st = B.LIB.qmoe_quant_act(x.ctypes.data, 4, 100, 0, out.ctypes.data, out.ctypes.data, None)

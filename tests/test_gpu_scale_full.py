@@ -205,6 +205,37 @@ def test_full_decode_q4_forced_overlap(full):
     assert err < TOL
 
 
+def test_full_decode_mfma(full):
+    """The matrix-core decode at the full shape: a q = 4 group meeting the
+    overlap criterion and one token; ids bit-exact, outputs within the
+    tolerance of the oracle and within 1e-5 of qmoe_decode_layer."""
+    spec, dl, L = full
+    for variant in range(64):
+        x4 = gen.q4_group(spec.hidden, seed=SEED, variant=variant)
+        idx_ref, _, _ = router.route(dl.w_router_host, x4, None, spec.topk)
+        if q4_overlap_ok(idx_ref):
+            break
+    else:
+        pytest.fail("no 4-token group met the overlap criterion")
+    for x in (x4, x4[1:2]):
+        xd = qm.device.to_device(x)
+        out = torch.empty_like(xd)
+        ws = dl.workspace(x.shape[0])
+        qm.qmoe_decode_layer_mfma(dl.desc, xd, out, ws)
+        torch.cuda.synchronize()
+        lay = qm.qmoe_workspace_layout(dl.desc, x.shape[0])
+        k = spec.topk
+        idx = ws[lay["idx"]: lay["idx"] + x.shape[0] * k * 4].cpu().numpy().view(np.int32).reshape(-1, k)
+        ref, idx_ref, _ = moe.moe_tokens(L, x)
+        assert np.array_equal(idx, idx_ref)
+        o = out.cpu().numpy()
+        err = moe.rel_l2(o, ref)
+        o2, _ = decode(dl, x)
+        print(f"mfma decode q={x.shape[0]}: rel_l2 {err:.2e}, vs dot4 path {moe.rel_l2(o, o2):.2e}")
+        assert err < TOL
+        assert moe.rel_l2(o, o2) < 1e-5
+
+
 def test_full_route_bit_exact_zipf(full):
     spec, dl, L = full
     bias = gen.zipf_bias(spec.n_experts)
