@@ -34,7 +34,7 @@ INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, published (TOPS)
 # HBM bytes per launch of the dominant decode q=1 kernel (k_gateup1<2>), from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs scaled by a 256 MiB device copy (profiles/hbm_traffic_decode_q1_prefill_8k.md). Must be
 # re-measured (or set to None) whenever that kernel changes.
-DOMINANT_Q1_TRAFFIC_BYTES = 31810712
+DOMINANT_Q1_TRAFFIC_BYTES = 31819695
 
 WORKLOAD = ("MoE decode layer q=1: hidden 4096, 256 routed experts, expert intermediate 2048, router W fp16 "
             "N(0,0.02) with softmax top-6, gate/up ROCmFP2 (4-entry per-expert codebooks), down ROCmFP3 "
