@@ -524,7 +524,7 @@ __global__ __launch_bounds__(1024) void k_gateupq2(DecodeArgs a) {
   constexpr int NBL = (FMT == 4) ? 1 : 2;
   constexpr int RPW = 2;
   constexpr int CPL = 2 * NBL;
-  __shared__ float s_a[4][32];
+  __shared__ float s_a2[2][4][32];   // SwiGLU rows of alternate items (see the item loop)
   __shared__ PlanLds P;
   __shared__ u32x4 s_xq[Q * 256];   // per token: 64 lanes x CPL pieces
   __shared__ float s_dx[Q * 128];   // per token: 64 lanes x NBL scales
@@ -624,8 +624,12 @@ __global__ __launch_bounds__(1024) void k_gateupq2(DecodeArgs a) {
           }
       }
     }
-    gateup_epilogue<Q, RPW>(a, mask, u, rb, ag, au, s_a);
-    __syncthreads();   // s_a is reused by the next item
+    // alternate items use alternate SwiGLU buffers, so no barrier is needed after
+    // the requantization: the next item's SwiGLU writes the other buffer, and the
+    // item after it passes the next item's barrier, which the requantizing waves
+    // reach only after finishing (q=4 42.35 -> 42.05 us in an interleaved
+    // comparison, same bits)
+    gateup_epilogue<Q, RPW>(a, mask, u, rb, ag, au, s_a2[((it - (int)blockIdx.x) / (int)gridDim.x) & 1]);
   }
 }
 
