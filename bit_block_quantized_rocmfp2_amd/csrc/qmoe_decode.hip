@@ -574,9 +574,32 @@ __global__ __launch_bounds__(1024) void k_gateupq2(DecodeArgs a) {
   const int b = lane * NBL;
   const bool ok = b < nb;
   const int bc = min(b, nb - NBL);
-  for (int it = blockIdx.x; it < U * nrb; it += gridDim.x) {
+  // Work units: the items of the full rounds whole, then the last round's items
+  // split by columns (each column's products, SwiGLU and requantization are
+  // independent), with the fewest columns per unit that leave every workgroup at
+  // most one unit, so that the last round does not keep a few workgroups busy
+  // with whole items while the rest wait.
+  const int NI = U * nrb, G = (int)gridDim.x;
+  const int full = NI - NI % G;
+  const int L = NI - full;
+  const int S = (L * Q <= G) ? 1 : (L * ((Q + 1) / 2) <= G) ? 2 : Q;   // columns per last-round unit
+  const int CG = (Q + S - 1) / S;                                        // column groups per item
+  const int nunits = full + L * CG;
+  int k = 0;   // units processed by this workgroup (alternate SwiGLU buffers)
+  for (int w = blockIdx.x; w < nunits; w += G) {
+    int it;
+    uint32_t cmask;
+    if (w < full) {
+      it = w;
+      cmask = 0xFu;
+    } else {
+      const int j = w - full;
+      it = full + j / CG;
+      cmask = ((1u << S) - 1u) << (S * (j % CG));
+    }
     const int u = it / nrb, rb = it % nrb;
-    const uint32_t mask = P.umask[u];
+    const uint32_t mask = P.umask[u] & cmask;
+    if (mask == 0u) continue;   // (uniform) no routed column in this group
     const int e = P.uid[u];
     const int row0 = rb * 32 + wave * RPW;
     const uint8_t* gbase = a.gate + (size_t)e * a.gu_stride;
@@ -624,12 +647,13 @@ __global__ __launch_bounds__(1024) void k_gateupq2(DecodeArgs a) {
           }
       }
     }
-    // alternate items use alternate SwiGLU buffers, so no barrier is needed after
-    // the requantization: the next item's SwiGLU writes the other buffer, and the
-    // item after it passes the next item's barrier, which the requantizing waves
+    // alternate units use alternate SwiGLU buffers, so no barrier is needed after
+    // the requantization: the next unit's SwiGLU writes the other buffer, and the
+    // unit after it passes the next unit's barrier, which the requantizing waves
     // reach only after finishing (q=4 42.35 -> 42.05 us in an interleaved
     // comparison, same bits)
-    gateup_epilogue<Q, RPW>(a, mask, u, rb, ag, au, s_a2[((it - (int)blockIdx.x) / (int)gridDim.x) & 1]);
+    gateup_epilogue<Q, RPW>(a, mask, u, rb, ag, au, s_a2[k & 1]);
+    ++k;
   }
 }
 
