@@ -585,34 +585,49 @@ __global__ __launch_bounds__(1024) void k_gateupq2(DecodeArgs a) {
   const int S = (L * Q <= G) ? 1 : (L * ((Q + 1) / 2) <= G) ? 2 : Q;   // columns per last-round unit
   const int CG = (Q + S - 1) / S;                                        // column groups per item
   const int nunits = full + L * CG;
-  int k = 0;   // units processed by this workgroup (alternate SwiGLU buffers)
-  for (int w = blockIdx.x; w < nunits; w += G) {
-    int it;
-    uint32_t cmask;
-    if (w < full) {
-      it = w;
-      cmask = 0xFu;
-    } else {
-      const int j = w - full;
-      it = full + j / CG;
-      cmask = ((1u << S) - 1u) << (S * (j % CG));
+  // the first non-empty unit at or after w (stride G), with its slot, row block
+  // and column mask; nunits when none is left
+  auto find_unit = [&](int w, int& u, int& rb, uint32_t& mask) -> int {
+    for (; w < nunits; w += G) {
+      int it;
+      uint32_t cmask;
+      if (w < full) {
+        it = w;
+        cmask = 0xFu;
+      } else {
+        const int j = w - full;
+        it = full + j / CG;
+        cmask = ((1u << S) - 1u) << (S * (j % CG));
+      }
+      u = it / nrb;
+      rb = it % nrb;
+      mask = P.umask[u] & cmask;
+      if (mask != 0u) return w;
     }
-    const int u = it / nrb, rb = it % nrb;
-    const uint32_t mask = P.umask[u] & cmask;
-    if (mask == 0u) continue;   // (uniform) no routed column in this group
+    return nunits;
+  };
+  Blocks<FMT, NBL> bg[RPW], bu[RPW];
+  uint32_t cbg[4], cbu[4];
+  // the wave's gate and up rows of a unit, every load issued (index clamped)
+  auto load_unit = [&](int u, int rb) {
     const int e = P.uid[u];
     const int row0 = rb * 32 + wave * RPW;
     const uint8_t* gbase = a.gate + (size_t)e * a.gu_stride;
     const uint8_t* ubase = a.up + (size_t)e * a.gu_stride;
-    uint32_t cbg[4], cbu[4];
     load_codebook<FMT>(a.cb_gate + ((size_t)e << FMT), cbg);
     load_codebook<FMT>(a.cb_up + ((size_t)e << FMT), cbu);
-    Blocks<FMT, NBL> bg[RPW], bu[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       bg[r].load(gbase + (size_t)(row0 + r) * a.gu_row_bytes, nb, bc);
       bu[r].load(ubase + (size_t)(row0 + r) * a.gu_row_bytes, nb, bc);
     }
+  };
+  int u = 0, rb = 0;
+  uint32_t mask = 0u;
+  int w = find_unit((int)blockIdx.x, u, rb, mask);
+  if (w < nunits) load_unit(u, rb);
+  int k = 0;   // units processed by this workgroup (alternate SwiGLU buffers)
+  while (w < nunits) {
     __builtin_amdgcn_sched_barrier(0);
     float ag[RPW][Q], au[RPW][Q];
 #pragma unroll
@@ -647,6 +662,13 @@ __global__ __launch_bounds__(1024) void k_gateupq2(DecodeArgs a) {
           }
       }
     }
+    // the next unit's weights are requested before this unit's epilogue, so that
+    // they stream during the SwiGLU, its barrier and the requantization (the
+    // last unit requests its own rows again: no branch around the loads)
+    int u2 = u, rb2 = rb;
+    uint32_t mask2 = 0u;
+    const int w2 = find_unit(w + G, u2, rb2, mask2);
+    load_unit(w2 < nunits ? u2 : u, w2 < nunits ? rb2 : rb);
     // alternate units use alternate SwiGLU buffers, so no barrier is needed after
     // the requantization: the next unit's SwiGLU writes the other buffer, and the
     // unit after it passes the next unit's barrier, which the requantizing waves
@@ -654,6 +676,10 @@ __global__ __launch_bounds__(1024) void k_gateupq2(DecodeArgs a) {
     // comparison, same bits)
     gateup_epilogue<Q, RPW>(a, mask, u, rb, ag, au, s_a2[k & 1]);
     ++k;
+    w = w2;
+    u = u2;
+    rb = rb2;
+    mask = mask2;
   }
 }
 
