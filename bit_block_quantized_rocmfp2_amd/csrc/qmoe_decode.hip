@@ -30,13 +30,18 @@
 //              (+ H32) for the down projection. One token: k_gateup1, one
 //              workgroup per item. Several tokens: one workgroup per CU walks
 //              the items (k_gateupq2 with the tokens' blocks in LDS when a row
-//              fits one pass of the lanes, k_gateupq otherwise).
+//              fits one pass of the lanes, k_gateupq otherwise); k_gateupq2
+//              splits the last round's items by columns and requests each next
+//              item's weights before the current item's epilogue.
 //   k_down     one workgroup per group of rows: the plan is read in one round
 //              trip, the rows of every planned expert are loaded together, per
 //              column contributions are accumulated per lane in ascending
 //              expert id with the routing weights, and reduced once. k_down1
 //              (one token) and k_downq (several) copy the routed activations
 //              to LDS once per workgroup; k_down serves the other shapes.
+//   k_gateupm, k_downm  the same layer with the expert products on the int8
+//              matrix cores (v_mfma_i32_4x4x4_16b_i8, the tokens as its four
+//              columns), behind qmoe_decode_layer_mfma.
 // Kernel boundaries make each launch's results visible to the next across the
 // 8 XCDs (separate L2 caches); no workgroup waits for another inside a launch.
 #include <hip/hip_runtime.h>
