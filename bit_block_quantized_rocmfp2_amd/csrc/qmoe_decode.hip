@@ -1432,37 +1432,55 @@ __global__ __launch_bounds__(256) void k_pf_down_small(SmallArgs sa) {
   const int nb = a.nb_i;
   uint32_t cb[4];
   load_codebook<FMT>(a.cb_down + ((size_t)e << FMT), cb);
-  for (int pass = 0; pass < kSmallDownPasses; ++pass) {
-    const int row = ((blockIdx.x * kSmallDownPasses + pass) * 4 + wave) * (64 >> lpr_log2) + sub;
-    const bool row_ok = row < a.hidden;
-    const uint8_t* wrow = a.down + (size_t)e * a.dn_stride + (size_t)min(row, a.hidden - 1) * a.dn_row_bytes;
-    float acc[Q];
+  // The expert's pairs' activations of the lane's blocks are the same for every
+  // pass (row group), so they are loaded once per chunk, and every pass's weight
+  // blocks are requested before any is used; each (row, pair) accumulates in
+  // the same order as a pass-by-pass walk.
+  constexpr int NP = kSmallDownPasses;
+  float acc[NP][Q];
 #pragma unroll
-    for (int t = 0; t < Q; ++t) acc[t] = 0.0f;
-    for (int c0 = 0; c0 < nb; c0 += lpr * NBL) {
-      const int b = c0 + sl * NBL;
-      if (row_ok && b < nb) {
-        Blocks<FMT, NBL> bl;
-        bl.load(wrow, nb, b);
-        Acts<NBL> act[Q];
+  for (int ps = 0; ps < NP; ++ps)
 #pragma unroll
-        for (int t = 0; t < Q; ++t)
-          if (t < cnt) act[t].load(sa.p.hq + (size_t)(pbase + t) * a.inter, sa.p.dh + (size_t)(pbase + t) * nb, b);
+    for (int t = 0; t < Q; ++t) acc[ps][t] = 0.0f;
+  for (int c0 = 0; c0 < nb; c0 += lpr * NBL) {
+    const int b = c0 + sl * NBL;
+    const int bcl = min(b, nb - NBL);
+    Acts<NBL> act[Q];
+#pragma unroll
+    for (int t = 0; t < Q; ++t) {
+      const int pt = pbase + min(t, cnt - 1);   // (clamped: pairs past cnt are not used)
+      act[t].load(sa.p.hq + (size_t)pt * a.inter, sa.p.dh + (size_t)pt * nb, bcl);
+    }
+    Blocks<FMT, NBL> bl[NP];
+#pragma unroll
+    for (int ps = 0; ps < NP; ++ps) {
+      const int row = ((blockIdx.x * NP + ps) * 4 + wave) * (64 >> lpr_log2) + sub;
+      bl[ps].load(a.down + (size_t)e * a.dn_stride + (size_t)min(row, a.hidden - 1) * a.dn_row_bytes, nb, bcl);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ps = 0; ps < NP; ++ps) {
+      const int row = ((blockIdx.x * NP + ps) * 4 + wave) * (64 >> lpr_log2) + sub;
+      if (row < a.hidden && b < nb) {
 #pragma unroll
         for (int i = 0; i < NBL; ++i) {
           uint32_t w[8];
-          bl.expand(i, cb, w);
-          const float sw = bl.scale(i);
+          bl[ps].expand(i, cb, w);
+          const float sw = bl[ps].scale(i);
 #pragma unroll
           for (int t = 0; t < Q; ++t)
-            if (t < cnt) acc[t] = fmaf((float)block_dot(w, act[t].q[i]), sw * act[t].d[i], acc[t]);
+            if (t < cnt) acc[ps][t] = fmaf((float)block_dot(w, act[t].q[i]), sw * act[t].d[i], acc[ps][t]);
         }
       }
     }
+  }
+#pragma unroll
+  for (int ps = 0; ps < NP; ++ps) {
+    const int row = ((blockIdx.x * NP + ps) * 4 + wave) * (64 >> lpr_log2) + sub;
 #pragma unroll
     for (int t = 0; t < Q; ++t) {
-      const float v = group_sum(acc[t], lpr);
-      if (t < cnt && sl == 0 && row_ok) {
+      const float v = group_sum(acc[ps][t], lpr);
+      if (t < cnt && sl == 0 && row < a.hidden) {
         const int pair = sa.p.pairs[pbase + t];
         sa.p.ypair[(size_t)pair * a.hidden + row] = v * sa.p.gw[pair];
       }
