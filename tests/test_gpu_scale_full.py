@@ -236,6 +236,38 @@ def test_full_decode_mfma(full):
         assert moe.rel_l2(o, o2) < 1e-5
 
 
+def test_full_decode_q4_column_units(full):
+    """q = 4 groups whose union of experts (U = 6, 7, 9, 10, 11: 384 .. 704
+    gate/up items of 32 rows) leaves a partial last round of items on the CUs,
+    which the q > 1 kernel splits by one or two columns per unit, or keeps whole:
+    every column equals the one-token call of its token bit for bit, and one
+    group is checked against the oracle."""
+    spec, dl, L = full
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    want = {6, 7, 9, 10, 11}
+    found = {}
+    for variant in range(200):
+        x = gen.q4_group(spec.hidden, seed=SEED, variant=variant)
+        idx_ref, _, _ = router.route(dl.w_router_host, x, None, spec.topk)
+        U = len(np.unique(idx_ref))
+        if U in want and U not in found and q4_overlap_ok(idx_ref):
+            found[U] = x
+        if len(found) == len(want):
+            break
+    assert found, "no group with a partial last round"
+    for U, x in sorted(found.items()):
+        items = U * (spec.inter // 32)
+        print(f"U={U}: {items} items, {items % cus} in the last round on {cus} CUs")
+        out4, _ = decode(dl, x)
+        for t in range(4):
+            out1, _ = decode(dl, x[t:t + 1])
+            assert np.array_equal(out4[t], out1[0])
+    U0, x0 = sorted(found.items())[0]
+    ref, _, _ = moe.moe_tokens(L, x0)
+    out4, _ = decode(dl, x0)
+    assert moe.rel_l2(out4, ref) < TOL
+
+
 def test_full_route_bit_exact_zipf(full):
     spec, dl, L = full
     bias = gen.zipf_bias(spec.n_experts)
