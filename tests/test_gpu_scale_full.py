@@ -236,6 +236,24 @@ def test_full_decode_mfma(full):
         assert moe.rel_l2(o, o2) < 1e-5
 
 
+@pytest.mark.parametrize("q", [2, 3])
+def test_full_decode_q2_q3(full, q):
+    """Two and three independent tokens at the full shape (up to 12 / 18 distinct
+    experts): ids bit-exact, output within the tolerance, every column equal to
+    the one-token call of its token bit for bit."""
+    spec, dl, L = full
+    x = gen.tokens(q, spec.hidden, seed=SEED + 7, stream=5)
+    out, idx = decode(dl, x)
+    ref, idx_ref, _ = moe.moe_tokens(L, x)
+    assert np.array_equal(idx, idx_ref)
+    err = moe.rel_l2(out, ref)
+    print(f"q={q}: distinct experts {len(np.unique(idx_ref))} rel_l2 {err:.2e}")
+    assert err < TOL
+    for t in range(q):
+        one, _ = decode(dl, x[t:t + 1])
+        assert np.array_equal(out[t], one[0])
+
+
 def test_full_decode_q4_column_units(full):
     """q = 4 groups whose union of experts (U = 6, 7, 9, 10, 11: 384 .. 704
     gate/up items of 32 rows) leaves a partial last round of items on the CUs,
