@@ -45,7 +45,7 @@ constexpr int kGroupThreads = 256;
 
 template <int FMT>
 constexpr int group_nbl() { return FMT == 4 ? 1 : 2; }
-inline int group_nbl_rt(int fmt) { return fmt == 4 ? 1 : 2; }
+[[maybe_unused]] inline int group_nbl_rt(int fmt) { return fmt == 4 ? 1 : 2; }   // (used by the debug build's checks)
 
 struct GroupItem {
   const uint8_t* w;
