@@ -538,7 +538,7 @@ def bench_dense(args, torch, qm, gen, dev, res):
             step()
         torch.cuda.synchronize()
         kern = {}
-        for n in ("group_fq", "group_quant", "group_mv"):   # one launch (group_fq) or two
+        for n in ("group_fq", "group_quant", "group_mvl", "group_mv"):   # one launch (group_fq) or two
             avg, cnt = kernel_avg_ms(qm, n)
             if cnt:
                 kern[n] = round(avg * 1e3, 2)

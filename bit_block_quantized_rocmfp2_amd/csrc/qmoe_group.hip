@@ -18,11 +18,15 @@
 //   k_group_quant  otherwise, every input of every matrix, one 32-block per
 //                  half-wave (the same IEEE operations as qmoe_quant_act), into
 //                  the workspace, then
-//   k_group_mv     every matrix's rows in one grid: each workgroup serves one
-//                  matrix, each wave one row unit (the rows that one wave
+//   k_group_mvl    every matrix's rows in one grid when each input (all
+//                  columns) holds at most 2048 blocks: each workgroup serves
+//                  one matrix and first copies its quantized input into LDS;
+//                  each wave takes one row unit (the rows that one wave
 //                  covers, 64 / lanes-per-row of them) at a time, in the lane
 //                  mapping and accumulation order of qmoe_matvec, so every
-//                  output equals qmoe_matvec's bit for bit (both forms).
+//                  output equals qmoe_matvec's bit for bit (every form);
+//   k_group_mv     the same with the input read from the workspace, for
+//                  longer inputs.
 // Each launch costs a fixed ~3 us on MI355X. (A one-launch form with a grid
 // barrier between the quantization and the products was measured slower: its
 // products cannot start before the barrier, so they no longer overlap the
@@ -146,6 +150,64 @@ __device__ __forceinline__ void group_wave(const GroupItem& it, int lw, const in
   }
 }
 
+// group_wave with the quantized input in LDS: the weights of UF chunks are
+// requested first, as there, but each block's activations are read from LDS
+// just before its products instead of being held in registers for the whole
+// step (LDS answers within the step; the registers go to the weights). The
+// products and additions are group_wave's, in its order.
+template <int FMT, int Q, int WPG, int UF>
+__device__ __forceinline__ void group_wave_lds(const GroupItem& it, int lw, const int8_t* xq, const float* dx) {
+  constexpr int NBL = group_nbl<FMT>();
+  const int lane = threadIdx.x & 63;
+  const int lpr_log2 = it.lpr_log2, lpr = 1 << lpr_log2;
+  const int sub = lane >> lpr_log2, sl = lane & (lpr - 1);
+  const int rpw = 64 >> lpr_log2;
+  const int nb = it.nb, W = it.nwg * WPG;
+  uint32_t cb[4];
+  load_codebook<FMT>(it.cb, cb);
+  for (int u = lw; u < it.units; u += W) {
+    const int64_t row = (int64_t)u * rpw + sub;
+    const bool ok = row < it.rows;
+    const uint8_t* rp = it.w + (size_t)(ok ? row : it.rows - 1) * it.row_bytes;
+    float acc[Q];
+#pragma unroll
+    for (int t = 0; t < Q; ++t) acc[t] = 0.0f;
+    for (int c0 = 0; c0 < nb; c0 += UF * lpr * NBL) {
+      Blocks<FMT, NBL> bl[UF];
+#pragma unroll
+      for (int c = 0; c < UF; ++c) bl[c].load(rp, nb, min(c0 + c * lpr * NBL + sl * NBL, nb - NBL));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < UF; ++c) {
+        const int b = c0 + c * lpr * NBL + sl * NBL;
+        if (ok && b < nb) {
+#pragma unroll
+          for (int i = 0; i < NBL; ++i) {
+            Acts<1> act[Q];
+#pragma unroll
+            for (int t = 0; t < Q; ++t) act[t].load(xq + (size_t)t * nb * 32, dx + (size_t)t * nb, b + i);
+            uint32_t w[8];
+            bl[c].expand(i, cb, w);
+            const float s = bl[c].scale(i);
+#pragma unroll
+            for (int t = 0; t < Q; ++t) {
+              const int p = block_dot(w, act[t].q[0]);
+              acc[t] = fmaf((float)p, s * act[t].d[0], acc[t]);
+            }
+            // one block's activations in registers at a time
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < Q; ++t) {
+      const float v = group_sum(acc[t], lpr);
+      if (sl == 0 && ok) it.y[(size_t)t * it.rows + row] = v;
+    }
+  }
+}
+
 template <int Q>
 __global__ __launch_bounds__(kGroupThreads) void k_group_mv(GroupArgs g) {
   int i = 0;
@@ -223,11 +285,65 @@ __global__ __launch_bounds__(kFqThreads, Q == 1 ? 6 : 4) void k_group_fq(GroupAr
   }
 }
 
+// Two-launch form with the quantized inputs in LDS, when every item's input
+// (all columns) holds at most kMvlMaxBlocks blocks: k_group_mv's row units, but
+// each workgroup first copies its item's quantized input and scales from the
+// workspace into LDS (all of a thread's loads issued before its stores), so
+// that the rows read the activations from LDS instead of from the caches: at
+// four columns a 16384-wide row re-reads 64 KB of them against its 8.5 KB of
+// weights. The rows' order of operations is group_wave's, so the outputs are
+// k_group_mv's bit for bit. (Dense 4-bit 4096 x 16384 + 3-bit 4096 x 2048 at
+// four columns: 23.6 -> 16.9 us per step against k_group_mv. Requesting each
+// wave's first weights before the copy, with the copy as direct global-to-LDS
+// loads, measured slower at four columns: 17.5 us.)
+constexpr int kMvlMaxBlocks = 2048;   // 64 KB of int8 blocks + 8 KB of scales: two workgroups per CU
+template <int Q> constexpr int mvl_uf() { return Q <= 2 ? 4 : 2; }   // chunks per step
+
+template <int Q>
+__global__ __launch_bounds__(kFqThreads, 4) void k_group_mvl(GroupArgs g) {
+  __shared__ u32x4 s_xq[2 * kMvlMaxBlocks];
+  __shared__ float s_dx[kMvlMaxBlocks];
+  int i = 0;
+#pragma unroll
+  for (int k = 1; k < kGroupMax; ++k)
+    if (k < g.n && (int)blockIdx.x >= g.it[k].wg0) i = k;
+  const GroupItem& it = g.it[i];
+  const int tid = threadIdx.x;
+  constexpr int NX = 2 * kMvlMaxBlocks / kFqThreads, ND = kMvlMaxBlocks / kFqThreads;
+  const int nx = 2 * Q * it.nb, nd = Q * it.nb;
+  const u32x4* gx = reinterpret_cast<const u32x4*>(it.xq);
+  u32x4 xv[NX];
+  float dv[ND];
+#pragma unroll
+  for (int k = 0; k < NX; ++k) xv[k] = gx[min(tid + k * kFqThreads, nx - 1)];
+#pragma unroll
+  for (int k = 0; k < ND; ++k) dv[k] = it.dx[min(tid + k * kFqThreads, nd - 1)];
+#pragma unroll
+  for (int k = 0; k < NX; ++k)
+    if (tid + k * kFqThreads < nx) s_xq[tid + k * kFqThreads] = xv[k];
+#pragma unroll
+  for (int k = 0; k < ND; ++k)
+    if (tid + k * kFqThreads < nd) s_dx[tid + k * kFqThreads] = dv[k];
+  __syncthreads();
+  constexpr int WPG = kFqThreads / 64;
+  const int lw = ((int)blockIdx.x - it.wg0) * WPG + (tid >> 6);
+  const int8_t* xq = reinterpret_cast<const int8_t*>(s_xq);
+  switch (it.fmt) {   // uniform over the workgroup
+    case 2: group_wave_lds<2, Q, WPG, mvl_uf<Q>()>(it, lw, xq, s_dx); break;
+    case 3: group_wave_lds<3, Q, WPG, mvl_uf<Q>()>(it, lw, xq, s_dx); break;
+    default: group_wave_lds<4, Q, WPG, mvl_uf<Q>()>(it, lw, xq, s_dx); break;
+  }
+}
+
 template <int Q>
 int launch_group(GroupArgs& g, hipStream_t s) {
   bool fq = Q <= 2;   // (three or four columns do not fit the one-launch form's registers)
-  for (int i = 0; i < g.n; ++i) fq = fq && Q * g.it[i].nb <= kFqMaxBlocks;
-  const int wpg = (fq ? kFqThreads : kGroupThreads) / 64;
+  bool mvl = true;
+  for (int i = 0; i < g.n; ++i) {
+    fq = fq && Q * g.it[i].nb <= kFqMaxBlocks;
+    mvl = mvl && Q * g.it[i].nb <= kMvlMaxBlocks;
+  }
+  const int wpg = (fq || mvl ? kFqThreads : kGroupThreads) / 64;
   int grid = 0;
   for (int i = 0; i < g.n; ++i) {   // one row unit per wave
     g.it[i].nwg = (g.it[i].units + wpg - 1) / wpg;
@@ -247,10 +363,15 @@ int launch_group(GroupArgs& g, hipStream_t s) {
       return launch_check("group_fq");
     }
   }
-  const int qgrid = (g.nblk + 2 * wpg - 1) / (2 * wpg);
+  constexpr int qwpg = kGroupThreads / 64;   // k_group_quant: two blocks per wave
+  const int qgrid = (g.nblk + 2 * qwpg - 1) / (2 * qwpg);
   launch_kernel("group_quant", k_group_quant, dim3(qgrid), dim3(kGroupThreads), s, g);
   int st = launch_check("group_quant");
   if (st) return st;
+  if (mvl) {
+    launch_kernel("group_mvl", k_group_mvl<Q>, dim3(grid), dim3(kFqThreads), s, g);
+    return launch_check("group_mvl");
+  }
   launch_kernel("group_mv", k_group_mv<Q>, dim3(grid), dim3(kGroupThreads), s, g);
   return launch_check("group_mv");
 }

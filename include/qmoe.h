@@ -245,7 +245,8 @@ typedef struct {
  * columns in one launch when ncols <= 2 and every input holds at most 512
  * blocks per call (ncols x k / 32; each workgroup quantizes its matrix's input
  * into LDS, then multiplies), else in two launches (all inputs quantized, then
- * all rows multiplied):
+ * all rows multiplied, each workgroup reading its matrix's quantized input from
+ * LDS when every input holds at most 2048 blocks per call):
  * the dense projections of a decode step ([Strix-284B], decode section: the
  * dense 4-bit weights of a step decoded once for all of its columns; [evox3],
  * table "The optimization ladder": the fused H32 matrix-vector path), where

@@ -118,23 +118,29 @@ def test_group_long_rows_and_bad_arguments():
     assert e.value.status == -3
 
 
-@pytest.mark.parametrize("ncols,k,one_launch", [(1, 16384, True), (2, 8192, True), (2, 8448, False),
-                                                 (3, 2048, False)])
-def test_group_launch_forms(ncols, k, one_launch):
+@pytest.mark.parametrize("ncols,k,form", [(1, 16384, "fq"), (2, 8192, "fq"), (2, 8448, "mvl"), (3, 2048, "mvl"),
+                                           (4, 16384, "mvl"), (4, 16640, "mv"), (1, 65536, "mvl"),
+                                           (1, 65792, "mv")])
+def test_group_launch_forms(ncols, k, form):
     """The one-launch form (inputs quantized into LDS by every workgroup) runs
-    for one or two columns when each input holds at most 512 blocks, the
-    two-launch form otherwise; both equal qmoe_matvec bit for bit, and both
-    leave the quantized inputs in the workspace."""
+    for one or two columns when each input holds at most 512 blocks (all
+    columns); otherwise the inputs are quantized by their own launch and the
+    products read them from LDS when each holds at most 2048 blocks, from the
+    workspace beyond that. Every form equals qmoe_matvec bit for bit and
+    leaves the quantized inputs in the workspace."""
     cases = [gen.matvec_case(2, 200, k, 4, seed=20, rot=1), gen.matvec_case(3, 64, 2048, 4, seed=21, rot=0)]
     mats, xs, ys, items = setup(cases, ncols)
     ref = reference(cases, mats, xs, ncols)
+    names = ("group_fq", "group_quant", "group_mvl", "group_mv")
     qm.qmoe_timing_enable(True)
     try:
         ws = run_group(items, ncols)
-        ran = {n: qm.qmoe_timing_read(n)[1] for n in ("group_fq", "group_quant", "group_mv")}
+        ran = {n: qm.qmoe_timing_read(n)[1] for n in names}
     finally:
         qm.qmoe_timing_enable(False)
-    assert (ran["group_fq"] == 1) == one_launch and (ran["group_mv"] == 1) == (not one_launch), ran
+    want = {"fq": {"group_fq": 1}, "mvl": {"group_quant": 1, "group_mvl": 1},
+            "mv": {"group_quant": 1, "group_mv": 1}}[form]
+    assert ran == {n: want.get(n, 0) for n in names}, ran
     for y, r in zip(ys, ref):
         assert np.array_equal(y.cpu().numpy(), r)
     c = cases[0]
