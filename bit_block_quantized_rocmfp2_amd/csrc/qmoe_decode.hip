@@ -223,34 +223,36 @@ __device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, in
       }
     }
     lds_barrier();
-    // wave 0 lists the plan once for the workgroup: lane s < U takes the s-th
-    // set bit of the union of the bitmaps (the distinct ids in ascending
-    // order) and its column mask; the items then read their slot from LDS
-    const int nw = (a.E + 31) >> 5;
+    // wave 0 lists the plan once for the workgroup: lane l holds bits
+    // 8l .. 8l + 7 of every token's bitmap (E <= 512) and of their union; the
+    // slot of its first expert is the number of set bits of the lanes below
+    // (eight ballots), and it lists its experts in ascending id order, so slot
+    // s holds the s-th distinct id and its column mask (the items then read
+    // their slot from LDS)
     if (wave == 0) {
-      uint32_t uw = 0;   // lane l < words: word l of the union bitmap
-      if (lane < nw)
+      const int wi = lane >> 2, sh = (lane & 3) * 8;
+      uint32_t tb[Q];
+      uint32_t ub = 0;
 #pragma unroll
-        for (int t = 0; t < Q; ++t)
-          if (t < a.q) uw |= P.bits[t][lane];
-      int es = -1, rs = lane, Ucount = 0;
-      for (int w = 0; w < nw; ++w) {
-        const uint32_t word = (uint32_t)__builtin_amdgcn_readlane(uw, w);
-        const int c = __popc(word);
-        if (es < 0 && rs < c) {
-          uint32_t x = word;
-          for (int i = 0; i < rs; ++i) x &= x - 1;
-          es = 32 * w + (int)__builtin_ctz(x);
-        }
-        if (es < 0) rs -= c;
-        Ucount += c;
+      for (int t = 0; t < Q; ++t) {
+        tb[t] = (t < a.q) ? (P.bits[t][wi] >> sh) & 0xFFu : 0u;
+        ub |= tb[t];
       }
-      uint32_t ms = 0;
-      float4 ws = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      if (lane < kPlanMax && es >= 0)
+      const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      int s = 0, Ucount = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint64_t bj = __ballot((ub >> j) & 1u);
+        s += __popcll(bj & lt);
+        Ucount += __popcll(bj);
+      }
+      for (uint32_t x = ub; x != 0u; x &= x - 1u, ++s) {
+        const int j = (int)__builtin_ctz(x), es = 8 * lane + j;
+        uint32_t ms = 0;
+        float4 ws = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
         for (int t = 0; t < Q; ++t)
-          if (t < a.q && (P.bits[t][es >> 5] >> (es & 31) & 1u)) {
+          if ((tb[t] >> j) & 1u) {
             ms |= 1u << t;
             if (write) {
               float wt = 0.0f;
@@ -263,13 +265,21 @@ __device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, in
               if (t == 3) ws.w = wt;
             }
           }
-      if (lane < kPlanMax) {
-        P.uid[lane] = es;
-        P.umask[lane] = ms;
+        P.uid[s] = es;   // (s < Ucount <= q * K <= kPlanMax)
+        P.umask[s] = ms;
         if (write) {
-          a.plan[kPlanIdOff + lane] = es;
-          a.plan[kPlanMaskOff + lane] = (int)ms;
-          reinterpret_cast<float4*>(a.plan + kPlanWOff)[lane] = ws;
+          a.plan[kPlanIdOff + s] = es;
+          a.plan[kPlanMaskOff + s] = (int)ms;
+          reinterpret_cast<float4*>(a.plan + kPlanWOff)[s] = ws;
+        }
+      }
+      if (lane >= Ucount && lane < kPlanMax) {   // the unused slots
+        P.uid[lane] = -1;
+        P.umask[lane] = 0u;
+        if (write) {
+          a.plan[kPlanIdOff + lane] = -1;
+          a.plan[kPlanMaskOff + lane] = 0;
+          reinterpret_cast<float4*>(a.plan + kPlanWOff)[lane] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
       }
       if (lane == 0) {
