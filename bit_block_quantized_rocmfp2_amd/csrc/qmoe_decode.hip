@@ -171,9 +171,12 @@ __device__ __forceinline__ void lds_barrier() {
 // and its column mask. `write` (one workgroup) also computes the routing
 // weights and stores the routing (idx, gw) and the plan (size, ids, masks,
 // weights per column).
-template <int Q>
+struct NoListingWork {
+  __device__ void operator()() const {}
+};
+template <int Q, typename ListingWork = NoListingWork>
 __device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, int u, bool write, uint32_t& mask,
-                                             int* U_out = nullptr) {
+                                             int* U_out = nullptr, ListingWork&& while_listing = ListingWork()) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   TopkPick p;
@@ -286,6 +289,8 @@ __device__ __forceinline__ int topk_and_plan(const DecodeArgs& a, PlanLds& P, in
         P.U = Ucount;
         if (write) a.plan[0] = Ucount;
       }
+    } else {
+      while_listing();   // the other waves' LDS work, ordered by the barrier below
     }
     lds_barrier();
     const int U = P.U;
@@ -565,26 +570,29 @@ __global__ __launch_bounds__(1024) void k_gateupq2(DecodeArgs a) {
   }
   uint32_t mask0;
   int U;
-  topk_and_plan<Q>(a, P, 0, blockIdx.x == 0, mask0, &U);
-  if (ct >= 0) {
+  // the copying waves store the tokens to LDS while wave 0 lists the plan; the
+  // selection's last barrier makes them visible to every wave
+  auto store_tokens = [&]() {
+    if (ct >= 0) {
 #pragma unroll
-    for (int k = 0; k < NXP; ++k) {
-      const int i = ct + NCP * k;
-      if (i < npx) {
-        const int t = i / (nb * 2), g = i % (nb * 2);
-        s_xq[t * 256 + (g % CPL) * 64 + g / CPL] = xv[k];
+      for (int k = 0; k < NXP; ++k) {
+        const int i = ct + NCP * k;
+        if (i < npx) {
+          const int t = i / (nb * 2), g = i % (nb * 2);
+          s_xq[t * 256 + (g % CPL) * 64 + g / CPL] = xv[k];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NDP; ++k) {
+        const int i = ct + NCP * k;
+        if (i < npd) {
+          const int t = i / nb, kk = i % nb;
+          s_dx[t * 128 + (kk % NBL) * 64 + kk / NBL] = dv[k];
+        }
       }
     }
-#pragma unroll
-    for (int k = 0; k < NDP; ++k) {
-      const int i = ct + NCP * k;
-      if (i < npd) {
-        const int t = i / nb, kk = i % nb;
-        s_dx[t * 128 + (kk % NBL) * 64 + kk / NBL] = dv[k];
-      }
-    }
-  }
-  __syncthreads();
+  };
+  topk_and_plan<Q>(a, P, 0, blockIdx.x == 0, mask0, &U, store_tokens);
   const int nrb = a.inter / 32;
   const int b = lane * NBL;
   const bool ok = b < nb;
