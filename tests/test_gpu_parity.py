@@ -414,6 +414,36 @@ def test_decode_top8(q):
     assert moe.rel_l2(out, ref) < TOL
 
 
+def test_decode_full_plan():
+    """Four tokens over 512 experts with top-8: up to 32 distinct experts, the
+    plan's capacity, listed from bitmaps whose set bits reach the last lanes.
+    The plan in the workspace is the sorted union of the routed ids, with each
+    slot's column mask and per-column routing weights; ids bit-exact and the
+    output within the bar."""
+    spec = gen.LayerSpec.tiny(n_experts=512, topk=8)
+    dl = qm.device.DeviceLayer(spec, seed=17)
+    x = gen.tokens(4, spec.hidden, seed=17)
+    out, ws = run_decode(dl, x)
+    ref, idx_ref, g_ref = moe.moe_tokens(oracle_layer(spec, 17, dl.w_router_host), x)
+    lay = qm.qmoe_workspace_layout(dl.desc, 4)
+    idx = ws[lay["idx"]: lay["idx"] + 4 * 4 * 8].cpu().numpy().view(np.int32).reshape(4, 8)
+    assert np.array_equal(idx, idx_ref)
+    assert moe.rel_l2(out, ref) < TOL
+    plan = ws[lay["plan"]: lay["plan"] + 4 * 256].cpu().numpy().view(np.int32)
+    union = np.unique(idx_ref)
+    U = int(plan[0])
+    assert U == len(union) and U >= 28   # (four random tokens rarely share an expert of 512)
+    assert np.array_equal(plan[1: 1 + U], union)
+    masks = plan[33: 33 + U]
+    w = plan[128: 128 + 4 * 32].view(np.float32).reshape(32, 4)
+    for s_, e in enumerate(union):
+        for t in range(4):
+            hit = np.nonzero(idx_ref[t] == e)[0]
+            assert ((masks[s_] >> t) & 1) == (len(hit) > 0)
+            assert abs(w[s_, t] - (g_ref[t, hit[0]] if len(hit) else 0.0)) < 1e-6
+    assert np.all(plan[1 + U: 33] == -1) and np.all(plan[33 + U: 65] == 0)
+
+
 @pytest.mark.parametrize("q,inter,topk", [(1, 768, 6), (3, 768, 6), (1, 2048, 6), (2, 2048, 6), (4, 2048, 6),
                                            (4, 2048, 8)])
 def test_decode_down_variants(q, inter, topk):
